@@ -1,0 +1,278 @@
+"""Benchmark of the MXFP8 o_proj chain on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|tiny|prefill|long]
+
+One step = one pass of the chain over one batch of synthetic tokens:
+grouped_fp8_einsum (wo_a, BF16 x quantized in the load path, MXFP8 epilogue)
+then fp8_gemm_nt (wo_b, BF16 out), replayed from a HIP graph.  Inputs are
+resident in HBM before the timed region.  Every step uses the next of R
+rotating copies of the inputs, weights and outputs (together >= 600 MB, more
+than the 256 MB Infinity Cache), so each step reads its weights cold, as the
+layers of a model do.
+
+Printed: one JSON line.  `value` is chain TFLOP/s at the configuration's token
+count; `ms_per_step` its time per call.  Besides the headline arm it reports the
+three-launch arm (standalone mxfp8_quantize first) and the unfused arm (BF16 z
+re-quantized by a separate launch), per-kernel durations from HIP events on the
+launch stream, the dominant kernel's roofline fraction, and the CPU oracle timed
+on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "o_proj chain µs/call + TFLOP/s (% HBM/FP8-MFMA roofline) at M=1..32768"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+ROTATE_BYTES = 600 << 20
+KERNEL_SOURCES = ["gemm.hip", "quantize.hip", "mx_device.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mxfp8_activation_quantization_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def chain_bytes(M, G, K, N, P):
+    """Algorithmic HBM bytes of each launch (weights once, activations once)."""
+    wa = G * N * K + G * N * (K // 128) * 4
+    wb = P * G * N + P * (G * N // 128) * 4
+    z_mx = M * (G * N + (G * N // 128) * 4)
+    return {
+        "einsum": M * G * K * 2 + wa + z_mx,              # BF16 x in, MXFP8 z out
+        "gemm": z_mx + wb + M * P * 2,                     # MXFP8 z in, BF16 out
+        "quantize_x": M * G * K * 2 + M * (G * K + (G * K // 128) * 4),
+    }
+
+
+def chain_flops(M, G, K, N, P):
+    return {"einsum": 2 * M * G * K * N, "gemm": 2 * M * G * N * P}
+
+
+def threads_used() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg_name, inp, budget_s=12.0):
+    """The oracle chain, as it stands, on a bounded sample of the same workload."""
+    from oracle import chain_ref as cr
+
+    w = cr.quantize_weights(inp["wo_a"], inp["wo_b"])
+    x = inp["x"]
+    rows = min(x.shape[0], 64)
+    sample = x[:rows]
+    G, N, K = w[0].shape
+    P = w[2].shape[0]
+    flop = 2 * rows * (G * K * N + G * N * P)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        cr.o_proj_chain(sample, *w)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    tflops = flop * reps / el / 1e12
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads_used(), "kind": "oracle",
+            "sample": f"{cfg_name}: first {rows} token rows, whole chain incl. weight dequantization, "
+                      f"{reps} repetitions in {el:.1f} s ({el / reps * 1e6:.0f} us/call)",
+            "host_cpu": cpu, "host_threads_visible": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--arms", default="fused,prequant,unfused")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the chain shards by token rows "
+              f"with no exchange, so N GPUs run N independent copies of this measurement.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth_inputs as si
+    import mxfp8_activation_quantization_amd as L
+
+    L.device_check()
+    cfg = si.CHAIN_CONFIGS[args.config]
+    S = cfg.shape
+    M, G, K, N, P = S.M, S.G, S.K, S.N, S.P
+    dev = torch.device("cuda", 0)
+    print(f"[bench] config {args.config}: M={M} G={G} K={K} N={N} P={P}; generating inputs", file=sys.stderr,
+          flush=True)
+    inp = si.chain_inputs(S, cfg.seed, cfg.outlier_rate)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x0 = to_dev(inp["x"])
+    wa_q0, wa_sf0 = L.quantize_weight(to_dev(inp["wo_a"]))
+    wb_q0, wb_sf0 = L.quantize_weight(to_dev(inp["wo_b"]))
+    set_bytes = x0.numel() * 2 + wa_q0.numel() + wb_q0.numel()
+    R = int(min(8, max(1, -(-ROTATE_BYTES // set_bytes))))
+
+    sets = []
+    for r in range(R):
+        s = {
+            "x": x0 if r == 0 else x0.clone(),
+            "wa_q": wa_q0 if r == 0 else wa_q0.clone(), "wa_sf": wa_sf0 if r == 0 else wa_sf0.clone(),
+            "wb_q": wb_q0 if r == 0 else wb_q0.clone(), "wb_sf": wb_sf0 if r == 0 else wb_sf0.clone(),
+            "z_q": torch.empty((M, G * N), dtype=torch.uint8, device=dev),
+            "z_sf": torch.empty((M, G * N // 128), dtype=torch.int32, device=dev),
+            "out": torch.empty((M, P), dtype=torch.bfloat16, device=dev),
+        }
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def launch_fused(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        L.grouped_fp8_einsum(s["x"], None, s["wa_q"], s["wa_sf"], out="mxfp8", z_q=s["z_q"], z_sf=s["z_sf"],
+                             stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        L.fp8_gemm_nt(s["z_q"], s["z_sf"], s["wb_q"], s["wb_sf"], d=s["out"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def launch_arm(arm, s):
+        if arm == "fused":
+            launch_fused(s)
+        else:
+            L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm, stream=stream)
+
+    def capture(arm):
+        graphs = []
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                launch_arm(arm, s)                      # warm: allocations of intermediate buffers
+                stream.synchronize()
+                with torch.cuda.graph(g, stream=stream):
+                    launch_arm(arm, s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    def time_graphs(graphs, steps, warmup):
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                graphs[i % R].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(steps):
+                graphs[i % R].replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+
+    arms = [a for a in args.arms.split(",") if a]
+    results = {}
+    for arm in arms:
+        graphs = capture(arm)
+        ms_ev, ms_wall = time_graphs(graphs, args.steps, args.warmup)
+        results[arm] = {"us_per_call": ms_ev * 1e3, "wall_us_per_call": ms_wall * 1e3}
+        print(f"[bench] arm {arm}: {ms_ev * 1e3:.2f} us/call (graph replay)", file=sys.stderr, flush=True)
+        del graphs
+
+    # per-kernel durations: HIP events on the launch stream around each kernel of the headline arm
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            launch_fused(sets[i % R])
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            launch_fused(sets[i % R], evs[i])
+    torch.cuda.synchronize()
+    t_einsum = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    t_gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+
+    flops = chain_flops(M, G, K, N, P)
+    nbytes = chain_bytes(M, G, K, N, P)
+    total_flop = flops["einsum"] + flops["gemm"]
+    head = results.get("fused", next(iter(results.values())))
+    us = head["us_per_call"]
+    value = total_flop / (us * 1e-6) / 1e12
+
+    dom = "einsum" if t_einsum >= t_gemm else "gemm"
+    t_dom = t_einsum if dom == "einsum" else t_gemm
+    hbm_bound = (total_flop / (nbytes["einsum"] + nbytes["gemm"])) < (FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3)
+    kern_name = {"einsum": "grouped_fp8_einsum", "gemm": "fp8_gemm_nt"}[dom]
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get(dom, {}).get("hbm_bytes_per_launch")
+    if hbm_bound:
+        ach = nbytes[dom] / (t_dom * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": traffic, "kernel": kern_name, "algorithmic_bytes_per_launch": nbytes[dom],
+                "avg_launch_us": t_dom}
+    else:
+        ach = flops[dom] / (t_dom * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / FP8_PEAK_TFLOPS, "traffic": traffic, "kernel": kern_name,
+                "algorithmic_flop_per_launch": flops[dom], "avg_launch_us": t_dom}
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8 (e4m3 x e4m3, fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": f"{args.config}: o_proj chain M={M} tokens, wo_a {G}x{K}->{N}, wo_b {G * N}->{P}",
+                   "M": M, "G": G, "K": K, "N": N, "P": P, "seed": cfg.seed,
+                   "x": "BF16 N(0,1)" + (f", {cfg.outlier_rate:g} of entries x100" if cfg.outlier_rate else ""),
+                   "weights": "MXFP8 of BF16 N(0,0.02)", "rotating_sets": R, "timing": "HIP graph replay"},
+        "us_per_call": us,
+        "arms_us_per_call": {a: r["us_per_call"] for a, r in results.items()},
+        "kernels_avg_us": {"grouped_fp8_einsum": t_einsum, "fp8_gemm_nt": t_gemm},
+        "hbm_roofline_frac_chain": (nbytes["einsum"] + nbytes["gemm"]) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "mfma_roofline_frac_chain": value / FP8_PEAK_TFLOPS,
+        "roofline": roof,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.config, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""MXFP8 o_proj chain for AMD Instinct MI355X (gfx950).
+
+Hand-written HIP kernels behind a C ABI (include/mxfp8.h), bound here with
+ctypes; torch supplies device memory and streams.
+
+    mxfp8_quantize      BF16 -> E4M3 codes + packed UE8M0 scales (one per 32 elements)
+    grouped_fp8_einsum  wo_a: grouped MXFP8 GEMM whose epilogue writes z as MXFP8 and/or BF16
+    fp8_gemm_nt         wo_b: MXFP8 GEMM with 1x32 scale blocks on both operands, BF16 out
+    o_proj_chain        the three in sequence on one stream
+"""
+from .binding import (  # noqa: F401
+    CHAIN_MODES,
+    MXFP8_ACT_BF16,
+    MXFP8_ACT_MXFP8,
+    MXFP8ArgumentError,
+    MXFP8Error,
+    device_check,
+    fp8_gemm_nt,
+    grouped_fp8_einsum,
+    lib,
+    mxfp8_quantize,
+    o_proj_chain,
+    quantize_weight,
+)

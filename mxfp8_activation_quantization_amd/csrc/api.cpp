@@ -1,0 +1,188 @@
+// C ABI of the MXFP8 o_proj chain library: argument validation, device check, dispatch.
+//
+// Every argument is checked on the host before the first HIP call, so argument
+// errors are reported the same way on a machine without a GPU.  The library
+// allocates nothing, never synchronizes, and keeps no state besides a per-device
+// cache of the architecture check.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/mxfp8.h"
+#include "launch.hpp"
+
+#define MX_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi) in bytes; empty when lo == hi
+};
+
+Range range2d(const void* base, int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+  Range r;
+  if (!base || rows <= 0 || cols <= 0) return r;
+  r.lo = reinterpret_cast<uintptr_t>(base);
+  r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + cols) * esize);
+  return r;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+std::atomic<int> g_arch_cache[256];  // 0 = unknown, 1 = gfx950, 2 = other
+
+int device_check() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MXFP8_ERR_DEVICE;
+  if (dev < 256) {
+    const int c = g_arch_cache[dev].load(std::memory_order_relaxed);
+    if (c == 1) return MXFP8_OK;
+    if (c == 2) return MXFP8_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXFP8_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 256) g_arch_cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MXFP8_OK : MXFP8_ERR_DEVICE;
+}
+
+// Activation operand: rows [0, M), `cols` columns.
+int check_act(int kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf, int64_t M,
+              int64_t cols) {
+  if (kind != MXFP8_ACT_BF16 && kind != MXFP8_ACT_MXFP8) return MXFP8_ERR_UNSUPPORTED;
+  if (ld_x < cols) return MXFP8_ERR_SHAPE;
+  const int64_t esize = kind == MXFP8_ACT_BF16 ? 2 : 1;
+  if ((ld_x * esize) % 16) return MXFP8_ERR_ALIGN;
+  if (kind == MXFP8_ACT_MXFP8 && ld_xsf < cols / 128) return MXFP8_ERR_SHAPE;
+  if (M == 0) return MXFP8_OK;
+  if (!x || (kind == MXFP8_ACT_MXFP8 && !x_sf)) return MXFP8_ERR_NULL;
+  if (!aligned(x, 16)) return MXFP8_ERR_ALIGN;
+  if (kind == MXFP8_ACT_MXFP8 && !aligned(x_sf, 4)) return MXFP8_ERR_ALIGN;
+  return MXFP8_OK;
+}
+
+Range act_range(int kind, const void* x, int64_t ld_x, int64_t M, int64_t cols) {
+  return range2d(x, M, cols, ld_x, kind == MXFP8_ACT_BF16 ? 2 : 1);
+}
+
+Range act_sf_range(int kind, const int32_t* x_sf, int64_t ld_xsf, int64_t M, int64_t cols) {
+  if (kind != MXFP8_ACT_MXFP8) return Range{};
+  return range2d(x_sf, M, cols / 128, ld_xsf, 4);
+}
+
+}  // namespace
+
+MX_API const char* mxfp8_status_string(int status) {
+  switch (status) {
+    case MXFP8_OK: return "ok";
+    case MXFP8_ERR_NULL: return "a required pointer is NULL";
+    case MXFP8_ERR_SHAPE: return "a size or stride is out of range or not a required multiple";
+    case MXFP8_ERR_ALIGN: return "a pointer or row stride breaks the alignment rules";
+    case MXFP8_ERR_UNSUPPORTED: return "unsupported activation kind or no output requested";
+    case MXFP8_ERR_ALIAS: return "an output overlaps an input or another output";
+    case MXFP8_ERR_DEVICE: return "the current HIP device is missing or is not gfx950";
+    case MXFP8_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+MX_API int mxfp8_version(void) { return 100; }
+
+MX_API int mxfp8_device_check(void) { return device_check(); }
+
+MX_API int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, void* q, int64_t ld_q,
+                          int32_t* sf, int64_t ld_sf, void* stream) {
+  if (M < 0 || K <= 0 || K % 128) return MXFP8_ERR_SHAPE;
+  if (ld_x < K || ld_q < K || ld_sf < K / 128) return MXFP8_ERR_SHAPE;
+  if ((ld_x * 2) % 16 || ld_q % 16) return MXFP8_ERR_ALIGN;
+  if (M == 0) return MXFP8_OK;
+  if (!x || !q || !sf) return MXFP8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return MXFP8_ERR_ALIGN;
+  const Range rx = range2d(x, M, K, ld_x, 2), rq = range2d(q, M, K, ld_q, 1),
+              rs = range2d(sf, M, K / 128, ld_sf, 4);
+  if (overlaps(rq, rx) || overlaps(rs, rx) || overlaps(rq, rs)) return MXFP8_ERR_ALIAS;
+  if (const int d = device_check(); d != MXFP8_OK) return d;
+  const hipError_t e = mx::launch_quantize(x, M, K, ld_x, q, ld_q, sf, ld_sf, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
+MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf,
+                              int64_t M, int64_t G, int64_t K, int64_t N, const void* w, const int32_t* w_sf,
+                              void* z_q, int64_t ld_z, int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb,
+                              void* stream) {
+  if (M < 0 || G < 1 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
+  if (G > 65535) return MXFP8_ERR_SHAPE;
+  const int64_t cols_in = G * K, cols_out = G * N;
+  if (int s = check_act(x_kind, x, ld_x, x_sf, ld_xsf, M, cols_in); s != MXFP8_OK) return s;
+  const bool want_mx = z_q != nullptr || z_sf != nullptr;
+  const bool want_bf = z_bf16 != nullptr;
+  if (!want_mx && !want_bf) return MXFP8_ERR_UNSUPPORTED;
+  if (want_mx && (!z_q || !z_sf)) return MXFP8_ERR_NULL;
+  if (want_mx && (ld_z < cols_out || ld_zsf < cols_out / 128)) return MXFP8_ERR_SHAPE;
+  if (want_mx && ld_z % 16) return MXFP8_ERR_ALIGN;
+  if (want_bf && ld_zb < cols_out) return MXFP8_ERR_SHAPE;
+  if (want_bf && (ld_zb * 2) % 16) return MXFP8_ERR_ALIGN;
+  if (!w || !w_sf) return MXFP8_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(w_sf, 4)) return MXFP8_ERR_ALIGN;
+  if (M == 0) return MXFP8_OK;
+  if (want_mx && (!aligned(z_q, 16) || !aligned(z_sf, 4))) return MXFP8_ERR_ALIGN;
+  if (want_bf && !aligned(z_bf16, 16)) return MXFP8_ERR_ALIGN;
+
+  const Range ins[4] = {act_range(x_kind, x, ld_x, M, cols_in), act_sf_range(x_kind, x_sf, ld_xsf, M, cols_in),
+                        range2d(w, G * N, K, K, 1), range2d(w_sf, G * N, K / 128, K / 128, 4)};
+  const Range outs[3] = {want_mx ? range2d(z_q, M, cols_out, ld_z, 1) : Range{},
+                         want_mx ? range2d(z_sf, M, cols_out / 128, ld_zsf, 4) : Range{},
+                         want_bf ? range2d(z_bf16, M, cols_out, ld_zb, 2) : Range{}};
+  for (const Range& o : outs) {
+    for (const Range& in : ins)
+      if (overlaps(o, in)) return MXFP8_ERR_ALIAS;
+  }
+  if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2]))
+    return MXFP8_ERR_ALIAS;
+  if (const int d = device_check(); d != MXFP8_OK) return d;
+
+  mx::GemmArgs p{};
+  p.x = x; p.ld_x = ld_x; p.x_sf = x_sf; p.ld_xsf = ld_xsf;
+  p.w = static_cast<const uint8_t*>(w); p.w_sf = w_sf;
+  p.M = M; p.N = N; p.K = K;
+  p.zq = static_cast<uint8_t*>(z_q); p.ld_zq = ld_z;
+  p.zsf = reinterpret_cast<uint8_t*>(z_sf); p.ld_zsf_bytes = ld_zsf * 4;
+  p.zb = static_cast<uint16_t*>(z_bf16); p.ld_zb = ld_zb;
+  const int out = (want_bf ? 1 : 0) | (want_mx ? 2 : 0);
+  const hipError_t e = mx::launch_gemm(p, G, x_kind == MXFP8_ACT_BF16, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
+MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf, int64_t M,
+                       int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
+                       void* stream) {
+  if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
+  if (int s = check_act(a_kind, a, ld_a, a_sf, ld_asf, M, K); s != MXFP8_OK) return s;
+  if (ld_d < N) return MXFP8_ERR_SHAPE;
+  if ((ld_d * 2) % 16) return MXFP8_ERR_ALIGN;
+  if (!b || !b_sf) return MXFP8_ERR_NULL;
+  if (!aligned(b, 16) || !aligned(b_sf, 4)) return MXFP8_ERR_ALIGN;
+  if (M == 0) return MXFP8_OK;
+  if (!d) return MXFP8_ERR_NULL;
+  if (!aligned(d, 16)) return MXFP8_ERR_ALIGN;
+  const Range out = range2d(d, M, N, ld_d, 2);
+  const Range ins[4] = {act_range(a_kind, a, ld_a, M, K), act_sf_range(a_kind, a_sf, ld_asf, M, K),
+                        range2d(b, N, K, K, 1), range2d(b_sf, N, K / 128, K / 128, 4)};
+  for (const Range& in : ins)
+    if (overlaps(out, in)) return MXFP8_ERR_ALIAS;
+  if (const int dc = device_check(); dc != MXFP8_OK) return dc;
+
+  mx::GemmArgs p{};
+  p.x = a; p.ld_x = ld_a; p.x_sf = a_sf; p.ld_xsf = ld_asf;
+  p.w = static_cast<const uint8_t*>(b); p.w_sf = b_sf;
+  p.M = M; p.N = N; p.K = K;
+  p.zb = static_cast<uint16_t*>(d); p.ld_zb = ld_d;
+  const hipError_t e = mx::launch_gemm(p, 1, a_kind == MXFP8_ACT_BF16, 1, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}

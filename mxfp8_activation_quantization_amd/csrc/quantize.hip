@@ -1,0 +1,81 @@
+// Standalone dynamic MXFP8 quantization of BF16 rows (HBM-bound streaming kernel).
+//
+// The quantize launch that vLLM PR #57977 ("[Perf][DSv4.1] Keep activations
+// MXFP8 between DeepGEMM kernels", Purpose) counts per decode step and that
+// PR #60118 ("[Perf][DSv4.1] MegaAttn: wo_a writes wo_b's MXFP8 input",
+// Claims) removes from the o_proj chain; here it also prepares the weights.
+//
+// Work unit: a 128-element span of one row (four 32-element blocks = one packed
+// scale word).  Sixteen consecutive lanes own a span; lane j = 4b + p loads the
+// 16 bytes holding elements [32b + 8p, 32b + 8p + 8), so a wave reads 1 KB of
+// contiguous BF16 per load.  The four lanes of a block combine their largest
+// magnitudes with two xor-shuffles, derive the block's scale, convert their
+// eight values and store 8 code bytes; lanes 0, 4, 8, 12 of the span hold the
+// four scale bytes, which lane 0 assembles into the packed word.
+#include "launch.hpp"
+#include "mx_device.hpp"
+
+namespace mx {
+
+constexpr int kQuantThreads = 256;
+constexpr int kSpansPerIter = 2;  // spans per 16-lane group per loop trip (loads in flight)
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
+    int32_t* __restrict__ sf, int64_t ld_sf, int64_t spans_per_row, int64_t total_spans) {
+  const int j = threadIdx.x & 15;
+  const int64_t groups = (int64_t)gridDim.x * (kQuantThreads / 16);
+  int64_t g = (int64_t)blockIdx.x * (kQuantThreads / 16) + (threadIdx.x >> 4);
+
+  for (int64_t s0 = g * kSpansPerIter; s0 < total_spans; s0 += groups * kSpansPerIter) {
+    uint4 v[kSpansPerIter];
+    int64_t row[kSpansPerIter], w[kSpansPerIter];
+#pragma unroll
+    for (int u = 0; u < kSpansPerIter; ++u) {
+      const int64_t s = s0 + u;
+      row[u] = s / spans_per_row;
+      w[u] = s - row[u] * spans_per_row;
+      if (s < total_spans)
+        v[u] = *reinterpret_cast<const uint4*>(x + row[u] * ld_x + w[u] * 128 + j * 8);
+      else
+        v[u] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kSpansPerIter; ++u) {
+      uint32_t m = amax_pair(amax_pair(amax_pair(amax_pair(0u, v[u].x), v[u].y), v[u].z), v[u].w);
+      m = fold_pair(m);
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1, 16));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2, 16));
+      const int e = scale_exp_from_amax(m);
+      const float scale = exp2_int(e);
+      const uint32_t c0 = encode4(v[u].x, v[u].y, scale);
+      const uint32_t c1 = encode4(v[u].z, v[u].w, scale);
+      const uint32_t sb = (uint32_t)(e + 127);
+      const uint32_t s1 = (uint32_t)__shfl((int)sb, 4, 16);
+      const uint32_t s2 = (uint32_t)__shfl((int)sb, 8, 16);
+      const uint32_t s3 = (uint32_t)__shfl((int)sb, 12, 16);
+      if (s0 + u < total_spans) {
+        *reinterpret_cast<uint2*>(q + row[u] * ld_q + w[u] * 128 + j * 8) = make_uint2(c0, c1);
+        if (j == 0) sf[row[u] * ld_sf + w[u]] = (int32_t)(sb | (s1 << 8) | (s2 << 16) | (s3 << 24));
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, void* q, int64_t ld_q,
+                           int32_t* sf, int64_t ld_sf, hipStream_t stream) {
+  const int64_t spans_per_row = K / 128;
+  const int64_t total = M * spans_per_row;
+  const int64_t groups_needed = (total + kSpansPerIter - 1) / kSpansPerIter;
+  const int64_t per_block = kQuantThreads / 16;
+  int64_t blocks = (groups_needed + per_block - 1) / per_block;
+  const int64_t cap = 256 * 32;  // enough resident waves to cover HBM latency; the rest loops
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), ld_x, static_cast<uint8_t*>(q), ld_q, sf, ld_sf,
+                     spans_per_row, total);
+  return hipGetLastError();
+}
+
+}  // namespace mx

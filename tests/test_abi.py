@@ -1,0 +1,140 @@
+"""Host-side tests of the C ABI (no GPU needed): the built library loads, exports
+every function include/mxfp8.h declares, and rejects bad arguments with the
+documented status codes before any HIP call.
+
+Pointers below are fake addresses: validation never dereferences them, and on
+a host without a gfx950 the only call that reaches HIP is the device check.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mxfp8.h")
+
+mx = pytest.importorskip("mxfp8_activation_quantization_amd",
+                         reason="libmxfp8.so is not built (run the build first)")
+from mxfp8_activation_quantization_amd import binding as B  # noqa: E402
+
+LIB = B.lib()
+HAVE_GPU = torch.cuda.is_available()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_chain_entry_points():
+    names = declared_functions()
+    for n in ("mxfp8_quantize", "grouped_fp8_einsum", "fp8_gemm_nt", "mxfp8_status_string",
+              "mxfp8_device_check", "mxfp8_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    for n in declared_functions():
+        assert hasattr(LIB, n), n
+        assert n in B.SIGNATURES, n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert LIB.mxfp8_status_string(s)
+    assert LIB.mxfp8_status_string(99) == b"unknown status"
+    assert LIB.mxfp8_version() >= 100
+
+
+@pytest.mark.skipif(HAVE_GPU, reason="a GPU is present")
+def test_device_check_without_gpu():
+    assert LIB.mxfp8_device_check() == B.MXFP8_ERR_DEVICE
+
+
+# fake, well-aligned addresses far apart
+X, Q, SF, W, WSF, Z, ZSF, ZB, D = (0x10000000 * (i + 1) for i in range(9))
+
+
+def quant(M=4, K=256, ld_x=None, ld_q=None, ld_sf=None, x=X, q=Q, sf=SF):
+    return LIB.mxfp8_quantize(x, M, K, ld_x or K, q, ld_q or K, sf, ld_sf or K // 128, None)
+
+
+def test_quantize_argument_errors():
+    assert quant(M=-1) == B.MXFP8_ERR_SHAPE
+    assert quant(K=0) == B.MXFP8_ERR_SHAPE
+    assert quant(K=96) == B.MXFP8_ERR_SHAPE
+    assert quant(ld_x=200) == B.MXFP8_ERR_SHAPE
+    assert quant(ld_sf=1) == B.MXFP8_ERR_SHAPE
+    assert quant(ld_x=260) == B.MXFP8_ERR_ALIGN           # 520-byte rows break 16-byte alignment
+    assert quant(ld_q=264) == B.MXFP8_ERR_ALIGN
+    assert quant(x=None) == B.MXFP8_ERR_NULL
+    assert quant(sf=None) == B.MXFP8_ERR_NULL
+    assert quant(x=X + 8) == B.MXFP8_ERR_ALIGN
+    assert quant(sf=SF + 2) == B.MXFP8_ERR_ALIGN
+    assert quant(q=X + 512) == B.MXFP8_ERR_ALIAS          # codes written into the input
+    assert quant(sf=Q + 64) == B.MXFP8_ERR_ALIAS
+    assert quant(M=0, x=None, q=None, sf=None) == B.MXFP8_OK   # empty batch is a no-op
+
+
+def einsum(kind=B.MXFP8_ACT_MXFP8, M=4, G=2, K=256, N=128, x=X, ld_x=None, x_sf=SF, ld_xsf=None, w=W,
+           w_sf=WSF, z=Z, ld_z=None, z_sf=ZSF, ld_zsf=None, zb=None, ld_zb=0):
+    return LIB.grouped_fp8_einsum(kind, x, ld_x or G * K, x_sf, ld_xsf or G * K // 128, M, G, K, N, w, w_sf,
+                                  z, ld_z or G * N, z_sf, ld_zsf or G * N // 128, zb, ld_zb, None)
+
+
+def test_einsum_argument_errors():
+    assert einsum(kind=7) == B.MXFP8_ERR_UNSUPPORTED
+    assert einsum(G=0) == B.MXFP8_ERR_SHAPE
+    assert einsum(N=96) == B.MXFP8_ERR_SHAPE                    # o_lora_rank % 128 gate
+    assert einsum(K=64) == B.MXFP8_ERR_SHAPE
+    assert einsum(ld_x=100) == B.MXFP8_ERR_SHAPE
+    assert einsum(z=None, z_sf=None, zb=None) == B.MXFP8_ERR_UNSUPPORTED
+    assert einsum(z_sf=None) == B.MXFP8_ERR_NULL
+    assert einsum(w=None) == B.MXFP8_ERR_NULL
+    assert einsum(x_sf=None) == B.MXFP8_ERR_NULL
+    assert einsum(ld_z=100) == B.MXFP8_ERR_SHAPE
+    assert einsum(ld_z=264) == B.MXFP8_ERR_ALIGN
+    assert einsum(w=W + 4) == B.MXFP8_ERR_ALIGN
+    assert einsum(z=X) == B.MXFP8_ERR_ALIAS
+    assert einsum(z_sf=Z + 16) == B.MXFP8_ERR_ALIAS
+    assert einsum(zb=ZSF, ld_zb=256) == B.MXFP8_ERR_ALIAS
+    assert einsum(kind=B.MXFP8_ACT_BF16, x_sf=None, ld_x=516) == B.MXFP8_ERR_ALIGN   # 1032-byte rows
+    assert einsum(M=0, x=None, z=Z, z_sf=ZSF) == B.MXFP8_OK
+
+
+@pytest.mark.skipif(HAVE_GPU, reason="a GPU is present")
+def test_valid_einsum_reports_missing_device():
+    assert einsum() == B.MXFP8_ERR_DEVICE
+    assert einsum(kind=B.MXFP8_ACT_BF16, x_sf=None) == B.MXFP8_ERR_DEVICE
+
+
+def gemm(kind=B.MXFP8_ACT_MXFP8, M=4, N=256, K=256, a=X, ld_a=None, a_sf=SF, ld_asf=None, b=W, b_sf=WSF, d=D,
+         ld_d=None):
+    return LIB.fp8_gemm_nt(kind, a, ld_a or K, a_sf, ld_asf or K // 128, M, N, K, b, b_sf, d, ld_d or N, None)
+
+
+def test_gemm_argument_errors():
+    assert gemm(M=-3) == B.MXFP8_ERR_SHAPE
+    assert gemm(N=100) == B.MXFP8_ERR_SHAPE
+    assert gemm(ld_d=100) == B.MXFP8_ERR_SHAPE
+    assert gemm(ld_d=260) == B.MXFP8_ERR_ALIGN
+    assert gemm(d=None) == B.MXFP8_ERR_NULL
+    assert gemm(b_sf=None) == B.MXFP8_ERR_NULL
+    assert gemm(d=W + 64) == B.MXFP8_ERR_ALIAS
+    assert gemm(kind=3) == B.MXFP8_ERR_UNSUPPORTED
+    assert gemm(M=0, a=None, d=None) == B.MXFP8_OK
+
+
+@pytest.mark.skipif(HAVE_GPU, reason="a GPU is present")
+def test_valid_gemm_reports_missing_device():
+    assert gemm() == B.MXFP8_ERR_DEVICE
+
+
+def test_binding_raises_value_error_on_argument_status():
+    with pytest.raises(ValueError):
+        B._check(B.MXFP8_ERR_SHAPE, "test")
+    with pytest.raises(RuntimeError):
+        B._check(B.MXFP8_ERR_DEVICE, "test")

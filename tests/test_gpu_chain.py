@@ -1,0 +1,280 @@
+"""GPU parity of grouped_fp8_einsum, fp8_gemm_nt and the o_proj chain against the CPU oracle.
+
+The shapes are the DeepSeek-V4.1-Flash TP1 o_proj of vLLM PR #60118
+("[Perf][DSv4.1] MegaAttn: wo_a writes wo_b's MXFP8 input", Validation):
+8 groups x 4096 -> 1024, then 8192 -> 5120; plus a tiny chain (2 x 256 -> 128,
+256 -> 256).  Bars:
+  * exact-arithmetic regime (small codes, every partial sum exact in fp32):
+    BF16 outputs, z codes and z scales bit-exact with the oracle;
+  * invariants from the pages, bitwise: the fused MXFP8 z equals the quantizer
+    applied to the same kernel's BF16 z (PR #60118, Tests); pre-quantized x
+    equals in-kernel quantization (PR #57977, Test Result); the fused and
+    unfused chains give identical outputs (PR #60118, Validation);
+  * against the independent float64 oracle: z codes within 1 E4M3 ulp on at
+    least 99.9% of elements, every z scale that differs explained by a block
+    maximum within one BF16 step of a power-of-two threshold;
+  * the wo_b GEMM fed the oracle's own z: BF16 output within 2e-2 of each row's
+    RMS (max |err| / RMS);
+  * the whole chain: |out - out64| <= 2e-2 * RMS(row) plus the propagation
+    through |wo_b| of the z deviations the z bar admits.  gfx950's FP8 MFMA
+    aligns the products of one dot product to the largest with about twelve
+    fractional bits, so a few BF16 z values land one rounding step away from
+    the float64 value and flip a code by one ulp; each such flip moves the
+    output by |dz| * |wo_b|, which this bound charges exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from oracle import chain_ref as cr
+from oracle import mxfp8_ref as mx
+from tests.gpu_common import bf16_to_dev, dev, i32_to_dev, mx_ulp_distance, row_rel_err, to_np, u8_to_dev
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mxfp8_activation_quantization_amd as m
+    m.device_check()
+    return m
+
+
+# --------------------------------------------------------------------------- exact regime
+
+SMALL_CODES = np.array([0x00, 0x38, 0xB8, 0x40, 0xC0, 0x30, 0xB0], dtype=np.uint8)   # 0, +-1, +-2, +-0.5
+
+
+def exact_operands(rng, rows, cols):
+    """Codes in {0, +-0.5, +-1, +-2} and scales 2**{-1,0,1}: every product is a multiple of 2**-4 with
+    magnitude <= 16, so sums over K <= 4096 need at most 20 bits and fp32 accumulates them exactly."""
+    q = rng.choice(SMALL_CODES, size=(rows, cols))
+    sb = rng.integers(126, 129, size=(rows, cols // 32)).astype(np.uint8)
+    return q, mx.pack_scales(sb)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (7, 256, 512), (33, 384, 1024), (130, 256, 4096),
+                                   (257, 128, 256)])
+def test_gemm_exact_regime_bitexact(lib, M, N, K):
+    rng = np.random.default_rng(1000 + M)
+    aq, asf = exact_operands(rng, M, K)
+    bq, bsf = exact_operands(rng, N, K)
+    d = lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(bq), i32_to_dev(bsf))
+    ref = mx.bf16_round(cr.gemm_nt(aq, asf, bq, bsf))
+    assert np.array_equal(to_np(d), ref)
+
+
+@pytest.mark.parametrize("M,G,K,N", [(4, 2, 256, 128), (45, 3, 512, 256), (96, 8, 128, 128)])
+def test_einsum_exact_regime_bitexact(lib, M, G, K, N):
+    rng = np.random.default_rng(2000 + M)
+    xq, xsf = exact_operands(rng, M, G * K)
+    wq, wsf = exact_operands(rng, G * N, K)
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(u8_to_dev(xq), i32_to_dev(xsf), u8_to_dev(wq.reshape(G, N, K)),
+                                            i32_to_dev(wsf.reshape(G, N, K // 128)), out="both")
+    z64 = cr.grouped_einsum(xq, xsf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N)
+    zb = mx.bf16_round(z64)
+    oq, osf = mx.quantize(zb)
+    assert np.array_equal(to_np(z_b), zb)
+    assert np.array_equal(to_np(z_q), oq)
+    assert np.array_equal(to_np(z_sf), osf)
+
+
+# --------------------------------------------------------------------------- configs
+
+class Case:
+    """Inputs, weights (GPU-quantized and oracle-quantized) for one chain configuration."""
+
+    def __init__(self, shape, seed, outlier_rate, lib):
+        print(f"case M={shape.M} G={shape.G} K={shape.K} N={shape.N} P={shape.P} seed={seed}", flush=True)
+        self.shape = shape
+        inp = si.chain_inputs(shape, seed, outlier_rate)
+        self.x_bits = inp["x"]
+        G, N, K = shape.G, shape.N, shape.K
+        # GPU path: the library's quantizer prepares the weights
+        self.wa_q, self.wa_sf = lib.quantize_weight(bf16_to_dev(inp["wo_a"]))
+        self.wb_q, self.wb_sf = lib.quantize_weight(bf16_to_dev(inp["wo_b"]))
+        # oracle path: its own quantizer
+        self.o_w = cr.quantize_weights(inp["wo_a"], inp["wo_b"])
+        self.x = bf16_to_dev(self.x_bits)
+        torch.cuda.synchronize()
+
+    def oracle(self, rows=None):
+        if rows is None:
+            return cr.o_proj_chain(self.x_bits, *self.o_w)
+        return cr.o_proj_chain_rows(self.x_bits, *self.o_w, rows=rows)
+
+
+_cases = {}
+
+
+def get_case(name, lib):
+    if name not in _cases:
+        if name == "ragged":
+            c = si.CHAIN_CONFIGS["decode"]
+            _cases[name] = Case(si.ChainShape(300, 8, 4096, 1024, 5120), c.seed, c.outlier_rate, lib)
+        else:
+            c = si.CHAIN_CONFIGS[name]
+            _cases[name] = Case(c.shape, c.seed, c.outlier_rate, lib)
+    return _cases[name]
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_weights_quantized_on_gpu_match_oracle(lib, name):
+    c = get_case(name, lib)
+    wa_q, wa_sf, wb_q, wb_sf = c.o_w
+    assert np.array_equal(to_np(c.wa_q), wa_q) and np.array_equal(to_np(c.wa_sf), wa_sf)
+    assert np.array_equal(to_np(c.wb_q), wb_q) and np.array_equal(to_np(c.wb_sf), wb_sf)
+
+
+def check_z_against_oracle(z_q, z_sf, z_b, ref):
+    """z codes within 1 ulp on >= 99.9%; scale mismatches only at threshold-straddling block maxima."""
+    gq, gsf, gb = to_np(z_q), to_np(z_sf), to_np(z_b)
+    d = mx_ulp_distance(gq, gsf, ref.z_q, ref.z_sf)
+    frac_ok = np.mean(d <= 1)
+    gs, os_ = mx.unpack_scales(gsf), mx.unpack_scales(ref.z_sf)
+    bad = np.argwhere(gs != os_)
+    for r, b in bad:
+        amax = np.max(np.abs(ref.z64[r, 32 * b:32 * b + 32]))
+        k = min(int(gs[r, b]), int(os_[r, b])) - 127
+        thr = 448.0 * 2.0 ** k
+        assert abs(int(gs[r, b]) - int(os_[r, b])) == 1
+        assert abs(amax - thr) <= thr * 2.0 ** -7, (r, b, amax, thr)
+    print(f"z: {frac_ok * 100:.4f}% within 1 ulp, {len(bad)} of {gs.size} scales differ (threshold cases)",
+          flush=True)
+    assert frac_ok >= 0.999
+    # BF16 z against float64 z: one BF16 rounding plus fp32 accumulation error
+    zg = mx.bf16_decode(gb)
+    rms = np.sqrt(np.mean(ref.z64 ** 2, axis=1, keepdims=True))
+    err = np.abs(zg - ref.z64) - np.abs(ref.z64) * 2.0 ** -8
+    assert np.all(err <= 1e-3 * rms)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_einsum_vs_oracle(lib, name):
+    c = get_case(name, lib)
+    ref = c.oracle()
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
+    check_z_against_oracle(z_q, z_sf, z_b, ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_fused_z_equals_quantized_own_bf16(lib, name):
+    c = get_case(name, lib)
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
+    oq, osf = mx.quantize(to_np(z_b))
+    assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf)
+    gq, gsf = lib.mxfp8_quantize(z_b)                       # the consumer's own quantizer on the device
+    assert torch.equal(gq, z_q) and torch.equal(gsf, z_sf)
+    # output mode does not change the accumulation
+    z_q2, z_sf2 = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="mxfp8")
+    z_b2 = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="bf16")
+    assert torch.equal(z_q2, z_q) and torch.equal(z_sf2, z_sf) and torch.equal(z_b2, z_b)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_prequantized_x_equals_in_kernel_quantization(lib, name):
+    c = get_case(name, lib)
+    xq, xsf = lib.mxfp8_quantize(c.x)
+    a = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
+    b = lib.grouped_fp8_einsum(xq, xsf, c.wa_q, c.wa_sf, out="both")
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    # same for the GEMM's activation operand
+    z_b = a[2]
+    zq, zsf = lib.mxfp8_quantize(z_b)
+    assert torch.equal(lib.fp8_gemm_nt(z_b, None, c.wb_q, c.wb_sf), lib.fp8_gemm_nt(zq, zsf, c.wb_q, c.wb_sf))
+
+
+def check_out_against_oracle(c, out, z_q, z_sf, ref):
+    """Chain output within 2e-2 * row RMS plus the propagated z deviations admitted by the z bar."""
+    o = mx.bf16_decode(to_np(out))
+    rms = np.sqrt(np.mean(ref.out64 ** 2, axis=1, keepdims=True))
+    dz = np.abs(mx.dequantize(to_np(z_q), to_np(z_sf)) - mx.dequantize(ref.z_q, ref.z_sf))
+    wb = np.abs(mx.dequantize(c.o_w[2], c.o_w[3]))
+    prop = dz @ wb.T
+    err = np.abs(o - ref.out64)
+    rel = np.max(err / rms, axis=1)
+    print(f"out: max |err|/RMS {rel.max():.4f} (p99 {np.quantile(rel, 0.99):.4f}); "
+          f"rows above {OUT_TOL}: {int(np.sum(rel > OUT_TOL))} of {len(rel)}; "
+          f"max z-flip propagation / RMS {np.max(prop / rms):.4f}", flush=True)
+    assert np.all(err <= OUT_TOL * rms + prop)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_gemm_stage_on_oracle_z(lib, name):
+    """wo_b alone, on the oracle's own MXFP8 z: max |err| / row RMS <= 2e-2."""
+    c = get_case(name, lib)
+    ref = c.oracle()
+    out = lib.fp8_gemm_nt(u8_to_dev(ref.z_q), i32_to_dev(ref.z_sf), c.wb_q, c.wb_sf)
+    rel = row_rel_err(to_np(out), ref.out64)
+    print(f"wo_b on oracle z: max |err|/RMS {rel.max():.4f}", flush=True)
+    assert rel.max() <= OUT_TOL
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_chain_vs_oracle_and_modes_identical(lib, name):
+    c = get_case(name, lib)
+    ref = c.oracle()
+    outs = {m: lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode=m) for m in lib.CHAIN_MODES}
+    again = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
+    assert torch.equal(outs["fused"], again)                 # deterministic
+    for m in lib.CHAIN_MODES:
+        assert torch.equal(outs[m], outs["fused"]), m
+    z_q, z_sf = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="mxfp8")
+    check_out_against_oracle(c, outs["fused"], z_q, z_sf, ref)
+
+
+@pytest.mark.parametrize("M", [1, 7, 33, 129, 300])
+def test_ragged_token_counts(lib, M):
+    c = get_case("ragged", lib)
+    x = c.x[:M]
+    out = lib.o_proj_chain(x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
+    rows = list(range(M))
+    ref = cr.o_proj_chain_rows(c.x_bits, *c.o_w, rows=rows)
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(x, None, c.wa_q, c.wa_sf, out="both")
+    check_z_against_oracle(z_q, z_sf, z_b, ref)
+    check_out_against_oracle(c, out, z_q, z_sf, ref)
+    # rows are independent: the first M rows of the 300-row batch give the same bytes
+    full = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
+    assert torch.equal(full[:M], out)
+
+
+def test_outputs_respect_strides_and_guards(lib):
+    c = get_case("tiny", lib)
+    M, G, N = c.shape.M, c.shape.G, c.shape.N
+    zq = torch.full((M, G * N + 32), 0xA5, dtype=torch.uint8, device=dev())
+    zsf = torch.full((M, G * N // 128 + 2), 0x5A5A5A5A, dtype=torch.int32, device=dev())
+    zb = torch.zeros((M, G * N + 24), dtype=torch.bfloat16, device=dev())
+    zb[:, G * N:] = 7.0
+    lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both", z_q=zq[:, :G * N], z_sf=zsf[:, :G * N // 128],
+                           z_bf16=zb[:, :G * N])
+    a_q, a_sf, a_b = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
+    assert torch.equal(zq[:, :G * N], a_q) and torch.equal(zsf[:, :G * N // 128], a_sf)
+    assert torch.equal(zb[:, :G * N], a_b)
+    assert bool((zq[:, G * N:] == 0xA5).all()) and bool((zsf[:, G * N // 128:] == 0x5A5A5A5A).all())
+    assert bool((zb[:, G * N:] == 7.0).all())
+
+
+@pytest.mark.parametrize("name", ["prefill", "long"])
+def test_large_configs_sampled_rows(lib, name):
+    c = get_case(name, lib)
+    M = c.shape.M
+    out = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.choice(M, 128, replace=False)]))
+    print(f"{name}: oracle on {len(rows)} sampled rows of {M}", flush=True)
+    ref = c.oracle(rows)
+    idx = torch.from_numpy(rows).to(dev())
+    check_z_against_oracle(z_q[idx], z_sf[idx], z_b[idx], ref)
+    check_out_against_oracle(c, out[idx], z_q[idx], z_sf[idx], ref)
+    out_oz = lib.fp8_gemm_nt(u8_to_dev(ref.z_q), i32_to_dev(ref.z_sf), c.wb_q, c.wb_sf)
+    assert row_rel_err(to_np(out_oz), ref.out64).max() <= OUT_TOL
+    # invariants at full size
+    zq2, zsf2 = lib.mxfp8_quantize(z_b)
+    assert torch.equal(zq2, z_q) and torch.equal(zsf2, z_sf)
+    del c.x
+    _cases.pop(name)
