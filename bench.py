@@ -35,7 +35,7 @@ METRIC = "o_proj chain µs/call + TFLOP/s (% HBM/FP8-MFMA roofline) at M=1..3276
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 ROTATE_BYTES = 600 << 20
-KERNEL_SOURCES = ["gemm.hip", "quantize.hip", "mx_device.hpp"]
+KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_skinny.hip", "gemm_common.hpp", "quantize.hip", "mx_device.hpp"]
 
 
 def kernel_source_hash() -> str:

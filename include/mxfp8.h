@@ -30,6 +30,14 @@
  *   - Data pointers must be 16-byte aligned and data row strides a multiple of
  *     16 bytes; scale pointers must be 4-byte aligned.
  *   - Outputs must not overlap inputs or each other (MXFP8_ERR_ALIAS).
+ *   - Workspace: the GEMM entry points may need device scratch for split-K
+ *     partial sums; the matching *_workspace_size() call gives the bytes for a
+ *     shape (0 = none needed, pointer may be NULL).  The caller owns it, zero-
+ *     fills it once before first use (256-byte aligned).  Its first 64 KiB hold
+ *     split-K arrival counters, which every call leaves at zero when it
+ *     completes; the rest is scratch.  Calls of any shape may therefore reuse one
+ *     workspace one after another (same stream), but calls that run
+ *     concurrently (other streams) must not share one.
  *   - Non-finite inputs are outside the contract (codes then unspecified).
  *   - Results are deterministic: the same inputs give the same bytes, and the
  *     kernel choice depends only on (M, G, N, K), never on the activation kind
@@ -52,7 +60,8 @@ typedef enum {
   MXFP8_ERR_UNSUPPORTED = 4,  /* unknown activation kind, or no output requested */
   MXFP8_ERR_ALIAS = 5,        /* an output overlaps an input or another output */
   MXFP8_ERR_DEVICE = 6,       /* the current HIP device is missing or is not gfx950 */
-  MXFP8_ERR_LAUNCH = 7        /* the kernel launch failed */
+  MXFP8_ERR_LAUNCH = 7,       /* the kernel launch failed */
+  MXFP8_ERR_WORKSPACE = 8     /* workspace missing, too small, or misaligned */
 } mxfp8_status;
 
 /* Activation kinds: the type tag of an activation operand.  A producer/consumer
@@ -106,6 +115,9 @@ int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x,
  *   z_bf16, ld_zb
  *           optional BF16 output [M][ld_zb] (G*N columns).
  * At least one of z_q / z_bf16 must be given (z_q and z_sf together).
+ *   workspace, workspace_bytes
+ *           split-K scratch, at least grouped_fp8_einsum_workspace_size(M, G, K, N)
+ *           bytes (see the conventions above).
  * K and N must be positive multiples of 128 (N % 128 == 0 keeps every scale
  * word of z inside one group: PR #60118, Details, the o_lora_rank % 128 gate).
  */
@@ -113,7 +125,11 @@ int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x
                        int64_t M, int64_t G, int64_t K, int64_t N,
                        const void* w, const int32_t* w_sf,
                        void* z_q, int64_t ld_z, int32_t* z_sf, int64_t ld_zsf,
-                       void* z_bf16, int64_t ld_zb, void* stream);
+                       void* z_bf16, int64_t ld_zb,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes grouped_fp8_einsum needs for this shape (0 = none); -1 for an invalid shape. */
+int64_t grouped_fp8_einsum_workspace_size(int64_t M, int64_t G, int64_t K, int64_t N);
 
 /*
  * fp8_gemm_nt -- the wo_b projection, recipe (1,1,32): both operands K-contiguous
@@ -123,12 +139,17 @@ int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x
  *   a_kind, a, ld_a, a_sf, ld_asf   activation rows m in [0, M), K columns (as in the einsum)
  *   b       E4M3 [N][K] bytes, contiguous      b_sf  int32 [N][K/128], contiguous
  *   d       BF16 [M][ld_d], N columns (output)
+ *   workspace, workspace_bytes   split-K scratch, at least fp8_gemm_nt_workspace_size(M, N, K) bytes
  * K and N must be positive multiples of 128.
  */
 int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf,
                 int64_t M, int64_t N, int64_t K,
                 const void* b, const int32_t* b_sf,
-                void* d, int64_t ld_d, void* stream);
+                void* d, int64_t ld_d,
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes fp8_gemm_nt needs for this shape (0 = none); -1 for an invalid shape. */
+int64_t fp8_gemm_nt_workspace_size(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

@@ -22,11 +22,13 @@ MXFP8_ERR_UNSUPPORTED = 4
 MXFP8_ERR_ALIAS = 5
 MXFP8_ERR_DEVICE = 6
 MXFP8_ERR_LAUNCH = 7
+MXFP8_ERR_WORKSPACE = 8
 
 MXFP8_ACT_BF16 = 0
 MXFP8_ACT_MXFP8 = 1
 
-_ARG_ERRORS = {MXFP8_ERR_NULL, MXFP8_ERR_SHAPE, MXFP8_ERR_ALIGN, MXFP8_ERR_UNSUPPORTED, MXFP8_ERR_ALIAS}
+_ARG_ERRORS = {MXFP8_ERR_NULL, MXFP8_ERR_SHAPE, MXFP8_ERR_ALIGN, MXFP8_ERR_UNSUPPORTED, MXFP8_ERR_ALIAS,
+               MXFP8_ERR_WORKSPACE}
 
 c_i64 = ctypes.c_int64
 c_int = ctypes.c_int
@@ -39,8 +41,11 @@ SIGNATURES = {
     "mxfp8_device_check": (c_int, []),
     "mxfp8_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "grouped_fp8_einsum": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
-                                   c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
-    "fp8_gemm_nt": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64, c_vp]),
+                                   c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "grouped_fp8_einsum_workspace_size": (c_i64, [c_i64, c_i64, c_i64, c_i64]),
+    "fp8_gemm_nt": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64,
+                            c_vp, c_i64, c_vp]),
+    "fp8_gemm_nt_workspace_size": (c_i64, [c_i64, c_i64, c_i64]),
 }
 
 
@@ -57,7 +62,7 @@ class MXFP8ArgumentError(MXFP8Error, ValueError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m mxfp8_activation_quantization_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python mxfp8_activation_quantization_amd/build.py` "
             "(there is no CPU or framework fallback)")
     # torch (imported above) has already loaded its HIP runtime; the library binds to the same
     # libamdhip64.so.7 by soname, so torch's streams and device pointers are valid in it.
@@ -98,6 +103,30 @@ def _rows(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise ValueError(f"{name}: expected a 2-D tensor with unit column stride")
     if not t.is_cuda:
         raise ValueError(f"{name}: expected a device tensor")
+
+
+# Split-K scratch: one zero-filled buffer per (device, stream), grown on demand.  The
+# kernels leave its counters at zero, so a buffer is reusable by later calls on
+# the same stream (stream order serializes them).
+_workspaces: dict = {}
+
+
+def workspace_for(nbytes: int, device: torch.device, stream_ptr: int) -> torch.Tensor | None:
+    if nbytes <= 0:
+        return None
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_ptr)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _ws_args(need: int, device, stream_ptr: int, workspace: torch.Tensor | None):
+    if need <= 0:
+        return None, 0
+    ws = workspace if workspace is not None else workspace_for(need, device, stream_ptr)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def device_check() -> None:
@@ -145,7 +174,7 @@ def _act_args(x: torch.Tensor, x_sf: torch.Tensor | None):
 
 def grouped_fp8_einsum(x: torch.Tensor, x_sf: torch.Tensor | None, w: torch.Tensor, w_sf: torch.Tensor, *,
                        out: str = "mxfp8", z_q: torch.Tensor | None = None, z_sf: torch.Tensor | None = None,
-                       z_bf16: torch.Tensor | None = None, stream=None):
+                       z_bf16: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """wo_a: z[m, g*N+n] = sum_k x[m, g*K+k] w[g, n, k].
 
     x: BF16 [M, G*K] (quantized in the kernel) or E4M3 uint8 [M, G*K] with x_sf int32 [M, G*K/128].
@@ -179,11 +208,13 @@ def grouped_fp8_einsum(x: torch.Tensor, x_sf: torch.Tensor | None, w: torch.Tens
         _rows(z_bf16, torch.bfloat16, "z_bf16")
     else:
         z_bf16 = None
+    sp = _stream(stream)
+    wsp, wsn = _ws_args(_lib.grouped_fp8_einsum_workspace_size(M, G, K, N), dev, sp, workspace)
     _check(_lib.grouped_fp8_einsum(kind, xp, ldx, xsfp, ldxsf, M, G, K, N, _ptr(w), _ptr(w_sf),
                                    _ptr(z_q), z_q.stride(0) if z_q is not None else 0,
                                    _ptr(z_sf), z_sf.stride(0) if z_sf is not None else 0,
                                    _ptr(z_bf16), z_bf16.stride(0) if z_bf16 is not None else 0,
-                                   _stream(stream)), "grouped_fp8_einsum")
+                                   wsp, wsn, sp), "grouped_fp8_einsum")
     if out == "mxfp8":
         return z_q, z_sf
     if out == "bf16":
@@ -194,7 +225,7 @@ def grouped_fp8_einsum(x: torch.Tensor, x_sf: torch.Tensor | None, w: torch.Tens
 # ----------------------------------------------------------------------------- gemm
 
 def fp8_gemm_nt(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_sf: torch.Tensor,
-                d: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                d: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """wo_b: d[m, n] = bf16(sum_k a[m, k] b[n, k]); a BF16 or E4M3 (+ a_sf), b uint8 [N, K] + b_sf int32 [N, K/128]."""
     if b.dim() != 2 or b.dtype != torch.uint8 or b_sf.dtype != torch.int32:
         raise ValueError("b must be uint8 [N, K] and b_sf int32 [N, K/128]")
@@ -206,8 +237,10 @@ def fp8_gemm_nt(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_s
     if d is None:
         d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     _rows(d, torch.bfloat16, "d")
+    sp = _stream(stream)
+    wsp, wsn = _ws_args(_lib.fp8_gemm_nt_workspace_size(M, N, K), a.device, sp, workspace)
     _check(_lib.fp8_gemm_nt(kind, ap, lda, asfp, ldasf, M, N, K, _ptr(b), _ptr(b_sf), _ptr(d), d.stride(0),
-                            _stream(stream)), "fp8_gemm_nt")
+                            wsp, wsn, sp), "fp8_gemm_nt")
     return d
 
 

@@ -1,6 +1,8 @@
 """Ahead-of-time build of libmxfp8.so for gfx950 with hipcc (in-tree, no JIT).
 
-    python -m mxfp8_activation_quantization_amd.build
+    python mxfp8_activation_quantization_amd/build.py
+
+(Run by path: importing the package loads the library this script builds.)
 
 Every call recompiles all sources (hipcc cross-compiles for gfx950 on a host
 without a GPU).  Objects go to ``_build/`` beside this file; the shared library
@@ -21,7 +23,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libmxfp8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -76,6 +76,18 @@ Range act_sf_range(int kind, const int32_t* x_sf, int64_t ld_xsf, int64_t M, int
   return range2d(x_sf, M, cols / 128, ld_xsf, 4);
 }
 
+// Checks the caller's workspace against the plan and points the kernel arguments into it.
+int bind_workspace(const mx::GemmPlan& plan, void* ws, int64_t ws_bytes, mx::GemmArgs& p, Range& r) {
+  r = Range{};
+  if (plan.workspace_bytes == 0) return MXFP8_OK;
+  if (!ws || ws_bytes < plan.workspace_bytes || !aligned(ws, 256)) return MXFP8_ERR_WORKSPACE;
+  p.ws_counters = static_cast<uint32_t*>(ws);
+  p.ws_partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.counter_bytes);
+  r.lo = reinterpret_cast<uintptr_t>(ws);
+  r.hi = r.lo + (uintptr_t)plan.workspace_bytes;
+  return MXFP8_OK;
+}
+
 }  // namespace
 
 MX_API const char* mxfp8_status_string(int status) {
@@ -88,6 +100,7 @@ MX_API const char* mxfp8_status_string(int status) {
     case MXFP8_ERR_ALIAS: return "an output overlaps an input or another output";
     case MXFP8_ERR_DEVICE: return "the current HIP device is missing or is not gfx950";
     case MXFP8_ERR_LAUNCH: return "kernel launch failed";
+    case MXFP8_ERR_WORKSPACE: return "workspace missing, too small, or misaligned";
     default: return "unknown status";
   }
 }
@@ -115,7 +128,7 @@ MX_API int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, voi
 MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf,
                               int64_t M, int64_t G, int64_t K, int64_t N, const void* w, const int32_t* w_sf,
                               void* z_q, int64_t ld_z, int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb,
-                              void* stream) {
+                              void* workspace, int64_t workspace_bytes, void* stream) {
   if (M < 0 || G < 1 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
   if (G > 65535) return MXFP8_ERR_SHAPE;
   const int64_t cols_in = G * K, cols_out = G * N;
@@ -145,9 +158,15 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
   }
   if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2]))
     return MXFP8_ERR_ALIAS;
+  mx::GemmArgs p{};
+  Range rw;
+  if (int s = bind_workspace(mx::plan_gemm(M, G, N, K), workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
+  for (const Range& o : outs)
+    if (overlaps(rw, o)) return MXFP8_ERR_ALIAS;
+  for (const Range& in : ins)
+    if (overlaps(rw, in)) return MXFP8_ERR_ALIAS;
   if (const int d = device_check(); d != MXFP8_OK) return d;
 
-  mx::GemmArgs p{};
   p.x = x; p.ld_x = ld_x; p.x_sf = x_sf; p.ld_xsf = ld_xsf;
   p.w = static_cast<const uint8_t*>(w); p.w_sf = w_sf;
   p.M = M; p.N = N; p.K = K;
@@ -161,7 +180,7 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
 
 MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf, int64_t M,
                        int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
-                       void* stream) {
+                       void* workspace, int64_t workspace_bytes, void* stream) {
   if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
   if (int s = check_act(a_kind, a, ld_a, a_sf, ld_asf, M, K); s != MXFP8_OK) return s;
   if (ld_d < N) return MXFP8_ERR_SHAPE;
@@ -176,13 +195,28 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
                         range2d(b, N, K, K, 1), range2d(b_sf, N, K / 128, K / 128, 4)};
   for (const Range& in : ins)
     if (overlaps(out, in)) return MXFP8_ERR_ALIAS;
+  mx::GemmArgs p{};
+  Range rw;
+  if (int s = bind_workspace(mx::plan_gemm(M, 1, N, K), workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
+  if (overlaps(rw, out)) return MXFP8_ERR_ALIAS;
+  for (const Range& in : ins)
+    if (overlaps(rw, in)) return MXFP8_ERR_ALIAS;
   if (const int dc = device_check(); dc != MXFP8_OK) return dc;
 
-  mx::GemmArgs p{};
   p.x = a; p.ld_x = ld_a; p.x_sf = a_sf; p.ld_xsf = ld_asf;
   p.w = static_cast<const uint8_t*>(b); p.w_sf = b_sf;
   p.M = M; p.N = N; p.K = K;
   p.zb = static_cast<uint16_t*>(d); p.ld_zb = ld_d;
   const hipError_t e = mx::launch_gemm(p, 1, a_kind == MXFP8_ACT_BF16, 1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
+MX_API int64_t grouped_fp8_einsum_workspace_size(int64_t M, int64_t G, int64_t K, int64_t N) {
+  if (M < 0 || G < 1 || G > 65535 || K <= 0 || K % 128 || N <= 0 || N % 128) return -1;
+  return mx::plan_gemm(M, G, N, K).workspace_bytes;
+}
+
+MX_API int64_t fp8_gemm_nt_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return -1;
+  return mx::plan_gemm(M, 1, N, K).workspace_bytes;
 }

@@ -1,0 +1,97 @@
+// Pieces shared by the GEMM kernels: the scaled MFMA, fragment assembly, and the
+// output epilogue of one 32 x 32 accumulator tile.
+//
+// gfx950 lane layout of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (checked on the device):
+//   operands: lane l = i + 32q holds row i, K bytes [16q, 16q+16) in dwords 0-3
+//             and [32+16q, 32+16q+16) in dwords 4-7 of a 64-deep K step, so
+//             bytes 0-15 of every lane belong to the step's first 32-block and
+//             bytes 16-31 to its second;
+//   scales:   the scale of (row i, 32-block b) is byte `opsel` of lane i + 32b;
+//   result:   lane l holds column l % 32, rows 8*(r/4) + 4*(l/32) + r%4, r < 16.
+// With the packed word of a row's four 128-K blocks shifted right by 8q, opsel 0
+// serves the first 64-deep half of a 128-K step and opsel 2 the second.
+//
+// The weights are always the A operand (rows = output columns n) and the
+// activations the B operand (columns = tokens m): a lane's 16 results then lie in
+// one 32-wide block of n for one token, shared with the partner lane l ^ 32.
+#pragma once
+
+#include "launch.hpp"
+#include "mx_device.hpp"
+
+namespace mx {
+
+constexpr int kThreads = 256;  // four waves per workgroup
+
+enum OutMode { OUT_BF16 = 1, OUT_MX = 2, OUT_BOTH = 3 };
+
+template <int OPSEL>
+__device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, sa, OPSEL, sb);
+}
+
+__device__ __forceinline__ v8i frag(const uint4& lo, const uint4& hi) {
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+__device__ __forceinline__ v16f zero16() {
+  v16f z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Stores one 32 (n) x 32 (m) accumulator tile: lane (i, q) holds token m and the
+// 16 columns nb + 8*(r/4) + 4q + r%4.  Every fp32 sum is rounded to BF16 (nearest
+// even); the MXFP8 form quantizes those BF16 values, block by 32 columns, with the
+// same rule as mxfp8_quantize.  All lanes must call this (it shuffles); `live`
+// gates the stores of tokens beyond M.
+template <int OUT>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f& acc, int64_t m, bool live, int64_t nb,
+                                           int q) {
+  uint32_t h[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) h[r] = bf16_rne(acc[r]);
+  if constexpr (OUT & OUT_BF16) {
+    if (live) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const uint2 v = make_uint2(h[4 * r4] | (h[4 * r4 + 1] << 16), h[4 * r4 + 2] | (h[4 * r4 + 3] << 16));
+        *reinterpret_cast<uint2*>(p.zb + m * p.ld_zb + nb + 8 * r4 + 4 * q) = v;
+      }
+    }
+  }
+  if constexpr (OUT & OUT_MX) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) am = max(am, h[r] & 0x7FFFu);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    const int e = scale_exp_from_amax(am);
+    const float scale = exp2_int(e);
+    if (live) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const uint32_t c = encode4(h[4 * r4] | (h[4 * r4 + 1] << 16), h[4 * r4 + 2] | (h[4 * r4 + 3] << 16), scale);
+        *reinterpret_cast<uint32_t*>(p.zq + m * p.ld_zq + nb + 8 * r4 + 4 * q) = c;
+      }
+      if (q == 0) p.zsf[m * p.ld_zsf_bytes + nb / 32] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// Maps a flat workgroup id to a work index so that each XCD (workgroups are
+// dispatched round-robin over the 8 XCDs) receives one contiguous range of work:
+// neighbouring tiles, which share activation rows, then share one L2.
+__device__ __forceinline__ int xcd_work_index(int id, int total) {
+  if (total % 8 != 0) return id;
+  return (id % 8) * (total / 8) + id / 8;
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream);
+hipError_t launch_gemm_skinny(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,
+                              hipStream_t stream);
+
+}  // namespace mx

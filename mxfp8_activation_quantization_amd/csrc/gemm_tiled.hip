@@ -1,4 +1,5 @@
-// Block-scaled FP8 GEMMs on gfx950's V_MFMA_SCALE_F32_32X32X64_F8F6F4.
+// Block-scaled FP8 GEMM, LDS-tiled variant for many tokens, on gfx950's
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4.
 //
 // One kernel family serves both projections of the o_proj chain:
 //   * grouped_fp8_einsum (wo_a): G groups, z[m, g*N+n] = sum_k x[m, g*K+k] w[g,n,k],
@@ -10,45 +11,24 @@
 // which the load path quantizes with the same rule as mxfp8_quantize (PR #57977,
 // Test Result: pre-quantized input is bit-identical to in-kernel quantization).
 //
-// MFMA roles: the weights are the instruction's A operand (rows = output
-// columns n) and the activations its B operand (columns = tokens m).  Then each
-// lane's accumulator holds 16 values of one token spread over one 32-wide block
-// of n, shared with exactly one partner lane (l ^ 32): a block's amax for the
-// fused MXFP8 epilogue is one cross-lane max.
-//
-// gfx950 lane layout (checked on the device):
-//   operands: lane l = i + 32q holds row i, K bytes [16q, 16q+16) in dwords 0-3
-//             and [32+16q, 32+16q+16) in dwords 4-7 of a 64-deep K step;
-//   scales:   the scale of (row i, 32-block b) is byte `opsel` of lane i + 32b;
-//   result:   lane l holds column l % 32, rows 8*(r/4) + 4*(l/32) + r%4, r < 16.
+// MFMA roles and lane layout: see gemm_common.hpp.
 //
 // Tiles: a block owns BN weight rows x BM tokens and walks K in steps of 128
 // (exactly one packed scale word per row).  Both operand tiles are staged in
 // LDS, 128 bytes per row with the 16-byte chunks XOR-swizzled by row to spread
 // the MFMA fragment reads over the banks; the scale words are staged beside them.
-#include "launch.hpp"
-#include "mx_device.hpp"
+#include "gemm_common.hpp"
 
 namespace mx {
 
-constexpr int kThreads = 256;  // four waves
-
 __device__ __forceinline__ int swz(int row, int chunk) { return (row * 8 + (chunk ^ (row & 7))) * 16; }
 
-template <int OPSEL>
-__device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, sa, OPSEL, sb);
-}
-
-// Reads the 32-byte fragment of LDS tile row `row` for K-substep KS and lane half q.
+// The 32-byte fragment of LDS tile row `row` for 64-deep half KS and lane half q.
 template <int KS>
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int q) {
   const uint4 lo = *reinterpret_cast<const uint4*>(tile + swz(row, 4 * KS + q));
   const uint4 hi = *reinterpret_cast<const uint4*>(tile + swz(row, 4 * KS + 2 + q));
-  v8i f;
-  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
-  return f;
+  return frag(lo, hi);
 }
 
 template <int BN_, int BM_, int WN_, int WM_>
@@ -59,8 +39,6 @@ struct TileCfg {
   static_assert(WAVES_N * WAVES_M == 4, "four waves per block");
   static_assert(BN % 32 == 0 && BM % 32 == 0, "32-row MFMA tiles");
 };
-
-enum OutMode { OUT_BF16 = 1, OUT_MX = 2, OUT_BOTH = 3 };
 
 template <class C, bool X_BF16, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
@@ -171,50 +149,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // ---- epilogue: fp32 -> BF16 (RNE) -> optional BF16 store and/or MXFP8 store
+  // ---- epilogue
 #pragma unroll
   for (int b = 0; b < C::TM; ++b) {
     const int64_t m = m0 + wm * C::WM + b * 32 + i;
-    const bool live = m < p.M;
 #pragma unroll
-    for (int a = 0; a < C::TN; ++a) {
-      const int64_t nb = g * p.N + n0 + wn * C::WN + a * 32;   // first output column of this 32-block
-      uint32_t h[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) h[r] = bf16_rne(acc[a][b][r]);
-      if constexpr (OUT & OUT_BF16) {
-        if (live) {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const uint2 v = make_uint2(h[4 * r4] | (h[4 * r4 + 1] << 16), h[4 * r4 + 2] | (h[4 * r4 + 3] << 16));
-            *reinterpret_cast<uint2*>(p.zb + m * p.ld_zb + nb + 8 * r4 + 4 * q) = v;
-          }
-        }
-      }
-      if constexpr (OUT & OUT_MX) {
-        uint32_t am = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am = max(am, h[r] & 0x7FFFu);
-        am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-        const int e = scale_exp_from_amax(am);
-        const float scale = exp2_int(e);
-        if (live) {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const uint32_t c = encode4(h[4 * r4] | (h[4 * r4 + 1] << 16), h[4 * r4 + 2] | (h[4 * r4 + 3] << 16), scale);
-            *reinterpret_cast<uint32_t*>(p.zq + m * p.ld_zq + nb + 8 * r4 + 4 * q) = c;
-          }
-          if (q == 0) p.zsf[m * p.ld_zsf_bytes + nb / 32] = (uint8_t)(e + 127);
-        }
-      }
-    }
+    for (int a = 0; a < C::TN; ++a)
+      store_tile<OUT>(p, acc[a][b], m, m < p.M, g * p.N + n0 + wn * C::WN + a * 32, q);
   }
 }
 
 // Tile configurations.  The choice depends only on (M, G, N, K), never on the
 // activation kind or the output mode, so every variant of one shape shares the
 // accumulation order.
-using CfgSmall = TileCfg<128, 32, 32, 32>;   // few tokens: four waves side by side along n
 using CfgLarge = TileCfg<128, 128, 64, 64>;  // many tokens: 2 x 2 waves, 64 x 64 each
 
 template <class C, bool X_BF16, int OUT>
@@ -236,10 +183,46 @@ static hipError_t dispatch_kind_out(const GemmArgs& p, int64_t G, bool x_bf16, i
   return launch_cfg<C, false, OUT_BOTH>(p, G, s);
 }
 
-hipError_t launch_gemm(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream) {
-  if (p.N % 128 != 0) return hipErrorInvalidValue;
-  if (p.M <= 32) return dispatch_kind_out<CfgSmall>(p, G, x_bf16, out, stream);
+hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream) {
   return dispatch_kind_out<CfgLarge>(p, G, x_bf16, out, stream);
+}
+
+// Kernel choice: a pure function of (M, G, N, K) -- never of the activation kind
+// or the output mode -- so those variants share one accumulation order.
+constexpr int64_t kSkinnyMaxTokens = 256;
+constexpr int64_t kSliceSteps = 8;            // 128-K steps per K slice of the skinny kernel
+// The workspace always starts with this many bytes of arrival counters, whatever the
+// shape, so one shape's partial tiles never land on another shape's counters when
+// calls share a workspace.
+constexpr int64_t kCounterBytes = 65536;
+
+GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K) {
+  GemmPlan pl{};
+  const int mt = M <= 32 ? 1 : 2;
+  const int chunks = (int)((M + 32 * mt - 1) / (32 * mt));
+  const int64_t tiles = G * (N / 64) * chunks;
+  pl.skinny = M <= kSkinnyMaxTokens && tiles * 4 <= kCounterBytes;
+  if (!pl.skinny) {
+    pl.workgroups = G * (N / CfgLarge::BN) * ((M + CfgLarge::BM - 1) / CfgLarge::BM);
+    return pl;
+  }
+  pl.mt = mt;
+  pl.chunks = chunks;
+  pl.n_tiles = (int)(N / 64);
+  pl.splits = (int)((K / 128 + kSliceSteps - 1) / kSliceSteps);
+  pl.workgroups = tiles * pl.splits;
+  if (pl.splits > 1 && M > 0) {
+    pl.counter_bytes = kCounterBytes;
+    pl.workspace_bytes = pl.counter_bytes + tiles * pl.splits * (int64_t)(2 * pl.mt * 16 * 64) * 4;
+  }
+  return pl;
+}
+
+hipError_t launch_gemm(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream) {
+  if (p.N % 128 != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
+  const GemmPlan plan = plan_gemm(p.M, G, p.N, p.K);
+  if (plan.skinny) return launch_gemm_skinny(p, plan, G, x_bf16, out, stream);
+  return launch_gemm_tiled(p, G, x_bf16, out, stream);
 }
 
 }  // namespace mx

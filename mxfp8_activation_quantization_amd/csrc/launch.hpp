@@ -23,12 +23,30 @@ struct GemmArgs {
   int64_t ld_zsf_bytes;
   uint16_t* zb;           // BF16 output [M][ld_zb] (or null)
   int64_t ld_zb;
+  uint32_t* ws_counters;  // split-K arrival counters (zero between calls), or null
+  float* ws_partials;     // split-K fp32 partial tiles, or null
 };
+
+// Kernel choice and scratch needs of one GEMM launch: a pure function of
+// (M, G, N, K).  `workspace_bytes` is 0 when no split-K reduction is needed.
+struct GemmPlan {
+  bool skinny;
+  int mt;                 // token tiles of 32 per workgroup (skinny)
+  int chunks;             // token chunks (skinny)
+  int n_tiles;            // 64-row weight tiles per group (skinny)
+  int splits;             // K splits (skinny)
+  int64_t workgroups;
+  int64_t counter_bytes;  // leading part of the workspace: one uint32 per (tile, chunk), 256-byte aligned
+  int64_t workspace_bytes;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K);
 
 hipError_t launch_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, void* q, int64_t ld_q,
                            int32_t* sf, int64_t ld_sf, hipStream_t stream);
 
-// out: 1 = BF16 only, 2 = MXFP8 only, 3 = both.
+// out: 1 = BF16 only, 2 = MXFP8 only, 3 = both.  p.ws_* must point into a
+// workspace of at least plan_gemm(...).workspace_bytes when that is non-zero.
 hipError_t launch_gemm(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream);
 
 }  // namespace mx

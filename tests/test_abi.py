@@ -79,10 +79,13 @@ def test_quantize_argument_errors():
     assert quant(M=0, x=None, q=None, sf=None) == B.MXFP8_OK   # empty batch is a no-op
 
 
+WS = 0x10000000 * 12
+
+
 def einsum(kind=B.MXFP8_ACT_MXFP8, M=4, G=2, K=256, N=128, x=X, ld_x=None, x_sf=SF, ld_xsf=None, w=W,
-           w_sf=WSF, z=Z, ld_z=None, z_sf=ZSF, ld_zsf=None, zb=None, ld_zb=0):
+           w_sf=WSF, z=Z, ld_z=None, z_sf=ZSF, ld_zsf=None, zb=None, ld_zb=0, ws=WS, ws_bytes=1 << 30):
     return LIB.grouped_fp8_einsum(kind, x, ld_x or G * K, x_sf, ld_xsf or G * K // 128, M, G, K, N, w, w_sf,
-                                  z, ld_z or G * N, z_sf, ld_zsf or G * N // 128, zb, ld_zb, None)
+                                  z, ld_z or G * N, z_sf, ld_zsf or G * N // 128, zb, ld_zb, ws, ws_bytes, None)
 
 
 def test_einsum_argument_errors():
@@ -112,8 +115,9 @@ def test_valid_einsum_reports_missing_device():
 
 
 def gemm(kind=B.MXFP8_ACT_MXFP8, M=4, N=256, K=256, a=X, ld_a=None, a_sf=SF, ld_asf=None, b=W, b_sf=WSF, d=D,
-         ld_d=None):
-    return LIB.fp8_gemm_nt(kind, a, ld_a or K, a_sf, ld_asf or K // 128, M, N, K, b, b_sf, d, ld_d or N, None)
+         ld_d=None, ws=WS, ws_bytes=1 << 30):
+    return LIB.fp8_gemm_nt(kind, a, ld_a or K, a_sf, ld_asf or K // 128, M, N, K, b, b_sf, d, ld_d or N, ws, ws_bytes,
+                           None)
 
 
 def test_gemm_argument_errors():
@@ -131,6 +135,29 @@ def test_gemm_argument_errors():
 @pytest.mark.skipif(HAVE_GPU, reason="a GPU is present")
 def test_valid_gemm_reports_missing_device():
     assert gemm() == B.MXFP8_ERR_DEVICE
+
+
+def test_workspace_sizes():
+    # one 1024-deep K slice needs no split-K scratch; deeper K does (decode range only)
+    assert LIB.grouped_fp8_einsum_workspace_size(64, 8, 1024, 1024) == 0
+    need = LIB.grouped_fp8_einsum_workspace_size(64, 8, 4096, 1024)
+    assert need > 0 and need % 256 == 0
+    assert LIB.fp8_gemm_nt_workspace_size(64, 5120, 8192) > 0
+    assert LIB.fp8_gemm_nt_workspace_size(4096, 5120, 8192) == 0        # many tokens: no split
+    assert LIB.fp8_gemm_nt_workspace_size(0, 5120, 8192) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(64, 8, 4000, 1024) == -1
+    assert LIB.fp8_gemm_nt_workspace_size(64, 100, 8192) == -1
+
+
+def test_workspace_errors():
+    need = LIB.fp8_gemm_nt_workspace_size(4, 256, 4096)
+    assert need > 0
+    assert gemm(K=4096, ws=None) == B.MXFP8_ERR_WORKSPACE
+    assert gemm(K=4096, ws_bytes=need - 1) == B.MXFP8_ERR_WORKSPACE
+    assert gemm(K=4096, ws=WS + 128) == B.MXFP8_ERR_WORKSPACE            # 256-byte alignment
+    assert gemm(K=4096, ws=D) == B.MXFP8_ERR_ALIAS                        # workspace over the output
+    assert einsum(K=4096, ws=X) == B.MXFP8_ERR_ALIAS                      # workspace over the input
+    assert gemm(K=512, ws=None, ws_bytes=0) != B.MXFP8_ERR_WORKSPACE      # one K slice: none needed
 
 
 def test_binding_raises_value_error_on_argument_status():

@@ -57,7 +57,7 @@ def exact_operands(rng, rows, cols):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (7, 256, 512), (33, 384, 1024), (130, 256, 4096),
-                                   (257, 128, 256)])
+                                   (257, 128, 256), (5, 128, 1152), (40, 256, 2176), (64, 512, 8192)])
 def test_gemm_exact_regime_bitexact(lib, M, N, K):
     rng = np.random.default_rng(1000 + M)
     aq, asf = exact_operands(rng, M, K)
@@ -67,7 +67,8 @@ def test_gemm_exact_regime_bitexact(lib, M, N, K):
     assert np.array_equal(to_np(d), ref)
 
 
-@pytest.mark.parametrize("M,G,K,N", [(4, 2, 256, 128), (45, 3, 512, 256), (96, 8, 128, 128)])
+@pytest.mark.parametrize("M,G,K,N", [(4, 2, 256, 128), (45, 3, 512, 256), (96, 8, 128, 128), (3, 2, 1152, 128),
+                                     (64, 2, 4096, 256)])
 def test_einsum_exact_regime_bitexact(lib, M, G, K, N):
     rng = np.random.default_rng(2000 + M)
     xq, xsf = exact_operands(rng, M, G * K)
@@ -80,6 +81,25 @@ def test_einsum_exact_regime_bitexact(lib, M, G, K, N):
     assert np.array_equal(to_np(z_b), zb)
     assert np.array_equal(to_np(z_q), oq)
     assert np.array_equal(to_np(z_sf), osf)
+
+
+def test_split_k_workspace_counters_return_to_zero(lib):
+    """The split-K arrival counters are back at zero after each call, so the workspace can be reused."""
+    from mxfp8_activation_quantization_amd import binding as B
+    rng = np.random.default_rng(77)
+    M, N, K = 48, 256, 4096
+    aq, asf = exact_operands(rng, M, K)
+    bq, bsf = exact_operands(rng, N, K)
+    need = B.lib().fp8_gemm_nt_workspace_size(M, N, K)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    outs = [lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(bq), i32_to_dev(bsf), workspace=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, outs[0]) for o in outs)
+    tiles = (N // 64) * 1
+    assert int(ws[:4 * tiles].view(torch.int32).abs().sum()) == 0
+    assert np.array_equal(to_np(outs[0]), mx.bf16_round(cr.gemm_nt(aq, asf, bq, bsf)))
 
 
 # --------------------------------------------------------------------------- configs
@@ -278,3 +298,28 @@ def test_large_configs_sampled_rows(lib, name):
     assert torch.equal(zq2, z_q) and torch.equal(zsf2, z_sf)
     del c.x
     _cases.pop(name)
+
+
+def test_shared_workspace_across_shapes(lib):
+    """One workspace reused by einsum and GEMM calls of different shapes keeps every result exact."""
+    from mxfp8_activation_quantization_amd import binding as B
+    rng = np.random.default_rng(91)
+    shapes = [(129, 8, 4096, 1024, 5120), (64, 8, 4096, 1024, 5120), (200, 2, 2048, 256, 640)]
+    need = max(max(B.lib().grouped_fp8_einsum_workspace_size(M, G, K, N),
+                   B.lib().fp8_gemm_nt_workspace_size(M, P, G * N)) for M, G, K, N, P in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    for rep in range(2):
+        for M, G, K, N, P in shapes:
+            xq, xsf = exact_operands(rng, M, G * K)
+            wq, wsf = exact_operands(rng, G * N, K)
+            bq, bsf = exact_operands(rng, P, G * N)
+            zb = lib.grouped_fp8_einsum(u8_to_dev(xq), i32_to_dev(xsf), u8_to_dev(wq.reshape(G, N, K)),
+                                        i32_to_dev(wsf.reshape(G, N, K // 128)), out="bf16", workspace=ws)
+            z64 = cr.grouped_einsum(xq, xsf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N)
+            assert np.array_equal(to_np(zb), mx.bf16_round(z64)), (rep, M)
+            zq = rng.choice(SMALL_CODES, size=(M, G * N))
+            zsf = mx.pack_scales(rng.integers(126, 129, size=(M, G * N // 32)).astype(np.uint8))
+            d = lib.fp8_gemm_nt(u8_to_dev(zq), i32_to_dev(zsf), u8_to_dev(bq), i32_to_dev(bsf), workspace=ws)
+            assert np.array_equal(to_np(d), mx.bf16_round(cr.gemm_nt(zq, zsf, bq, bsf))), (rep, M)
+    torch.cuda.synchronize()
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
