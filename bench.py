@@ -104,6 +104,77 @@ def cpu_baseline(cfg_name, inp, budget_s=12.0):
             "host_cpu": cpu, "host_threads_visible": len(os.sched_getaffinity(0))}
 
 
+def copy_calibration(torch, mib):
+    """A plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read for it calibrates them."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 5}), flush=True)
+
+
+def time_arm_graphs(torch, graphs, stream, steps, warmup):
+    """Average µs per replay of a list of captured graphs, replayed round-robin on `stream`."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def sweep(torch, L, Ms, dims, w, stream, args):
+    """Fused and prequant chain µs/call over token counts, weights rotated as in the headline run."""
+    G, K, N, P = dims
+    out = []
+    gen = torch.Generator(device="cuda")
+    for M in Ms:
+        gen.manual_seed(20260100 + M)
+        x = torch.randn((M, G * K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        set_bytes = x.numel() * 2 + w["wa_q"].numel() + w["wb_q"].numel()
+        R = int(min(8, max(1, -(-ROTATE_BYTES // set_bytes))))
+        sets = [{"x": x if r == 0 else x.clone(),
+                 "wa_q": w["wa_q"].clone(), "wa_sf": w["wa_sf"].clone(),
+                 "wb_q": w["wb_q"].clone(), "wb_sf": w["wb_sf"].clone()} for r in range(R)]
+        res = {"M": M}
+        for arm in ("fused", "prequant"):
+            graphs = []
+            for s in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(stream):
+                    L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm, stream=stream)
+                    stream.synchronize()
+                    with torch.cuda.graph(g, stream=stream):
+                        L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm,
+                                       stream=stream)
+                graphs.append(g)
+            steps = max(5, min(args.steps, int(2e5 // max(1, M))))
+            res[f"{arm}_us"] = time_arm_graphs(torch, graphs, stream, steps, min(args.warmup, steps))
+            del graphs
+        flop = sum(chain_flops(M, G, K, N, P).values())
+        nb = chain_bytes(M, G, K, N, P)
+        us = min(res["fused_us"], res["prequant_us"])
+        res["tflops_fused"] = flop / (res["fused_us"] * 1e-6) / 1e12
+        res["hbm_frac_fused"] = (nb["einsum"] + nb["gemm"]) / (res["fused_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+        res["mfma_frac_fused"] = res["tflops_fused"] / FP8_PEAK_TFLOPS
+        res["best_us"] = us
+        print(f"[bench] sweep M={M}: fused {res['fused_us']:.2f} us, prequant {res['prequant_us']:.2f} us, "
+              f"{res['tflops_fused']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        out.append(res)
+        del sets, x
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +183,11 @@ def main():
     ap.add_argument("--config", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--arms", default="fused,prequant,unfused")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated token counts: also time the fused and prequant chains at each "
+                         "(decode-config weights, x drawn on the device) and report them under 'sweep'")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB 5 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the chain shards by token rows "
@@ -119,6 +195,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_mib:
+        copy_calibration(torch, args.copy_mib)
+        return
 
     import synth_inputs as si
     import mxfp8_activation_quantization_amd as L
@@ -268,6 +348,9 @@ def main():
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if args.sweep:
+        line["sweep"] = sweep(torch, L, [int(v) for v in args.sweep.split(",") if v], (G, K, N, P),
+                              sets[0], stream, args)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.config, inp)
