@@ -29,6 +29,9 @@
  *     output is touched.  M == 0 is a valid no-op (MXFP8_OK).
  *   - Data pointers must be 16-byte aligned and data row strides a multiple of
  *     16 bytes; scale pointers must be 4-byte aligned.
+ *   - GEMM size limits (32-bit tile addressing): K of a group <= 2^22, activation
+ *     row strides <= 2^23 bytes (scale rows <= 2^16 bytes); otherwise
+ *     MXFP8_ERR_SHAPE.
  *   - Outputs must not overlap inputs or each other (MXFP8_ERR_ALIAS).
  *   - Workspace: the GEMM entry points may need device scratch for split-K
  *     partial sums; the matching *_workspace_size() call gives the bytes for a

@@ -11,6 +11,7 @@ lands next to the Python binding, which loads it from there.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -49,9 +50,24 @@ def hipcc() -> str:
 
 def _run(cmd: list[str]) -> None:
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
+    lines = [l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l]
     if proc.returncode != 0:
-        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n" + "\n".join(lines))
+    # Every kernel must fit its registers: register spills go to scratch memory,
+    # cost bandwidth, and spill code inside lane-masked regions has produced wrong
+    # results.  The resource remarks name each kernel and its scratch bytes.
+    spilled, current = [], None
+    for l in lines:
+        m = re.search(r"Function Name: (\S+)", l)
+        if m:
+            current = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", l)
+        if m and int(m.group(1)) > 0:
+            spilled.append(f"{current}: {m.group(1)} bytes/lane")
+    if spilled:
+        raise RuntimeError("kernels spill registers to scratch:\n  " + "\n  ".join(spilled))
+    out = "\n".join(l for l in lines if "remark:" not in l and "-Rpass-analysis" not in l
+                    and not re.match(r"^\s*(\d+\s*)?\|", l))
     if out.strip():
         print(out, file=sys.stderr)
 
@@ -64,7 +80,7 @@ def build(verbose: bool = False) -> str:
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
         cmds.append([cc, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 1)) as ex:

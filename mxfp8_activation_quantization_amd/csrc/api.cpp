@@ -52,12 +52,19 @@ int device_check() {
   return ok ? MXFP8_OK : MXFP8_ERR_DEVICE;
 }
 
+// The GEMM kernels address one tile of up to 256 rows with 32-bit byte offsets:
+// row strides and the reduction depth are capped so that 256 rows always fit.
+constexpr int64_t kMaxRowBytes = int64_t(1) << 23;     // activation row stride, bytes
+constexpr int64_t kMaxDepth = int64_t(1) << 22;         // K of one group
+
 // Activation operand: rows [0, M), `cols` columns.
 int check_act(int kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf, int64_t M,
               int64_t cols) {
   if (kind != MXFP8_ACT_BF16 && kind != MXFP8_ACT_MXFP8) return MXFP8_ERR_UNSUPPORTED;
   if (ld_x < cols) return MXFP8_ERR_SHAPE;
   const int64_t esize = kind == MXFP8_ACT_BF16 ? 2 : 1;
+  if (ld_x * esize > kMaxRowBytes) return MXFP8_ERR_SHAPE;
+  if (kind == MXFP8_ACT_MXFP8 && ld_xsf * 4 > kMaxRowBytes / 128) return MXFP8_ERR_SHAPE;
   if ((ld_x * esize) % 16) return MXFP8_ERR_ALIGN;
   if (kind == MXFP8_ACT_MXFP8 && ld_xsf < cols / 128) return MXFP8_ERR_SHAPE;
   if (M == 0) return MXFP8_OK;
@@ -130,7 +137,7 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
                               void* z_q, int64_t ld_z, int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb,
                               void* workspace, int64_t workspace_bytes, void* stream) {
   if (M < 0 || G < 1 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
-  if (G > 65535) return MXFP8_ERR_SHAPE;
+  if (G > 65535 || K > kMaxDepth || M > INT32_MAX || G * N > INT32_MAX) return MXFP8_ERR_SHAPE;
   const int64_t cols_in = G * K, cols_out = G * N;
   if (int s = check_act(x_kind, x, ld_x, x_sf, ld_xsf, M, cols_in); s != MXFP8_OK) return s;
   const bool want_mx = z_q != nullptr || z_sf != nullptr;
@@ -182,6 +189,7 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
                        int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
                        void* workspace, int64_t workspace_bytes, void* stream) {
   if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
+  if (K > kMaxDepth || M > INT32_MAX || N > INT32_MAX) return MXFP8_ERR_SHAPE;
   if (int s = check_act(a_kind, a, ld_a, a_sf, ld_asf, M, K); s != MXFP8_OK) return s;
   if (ld_d < N) return MXFP8_ERR_SHAPE;
   if ((ld_d * 2) % 16) return MXFP8_ERR_ALIGN;
@@ -213,10 +221,12 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
 
 MX_API int64_t grouped_fp8_einsum_workspace_size(int64_t M, int64_t G, int64_t K, int64_t N) {
   if (M < 0 || G < 1 || G > 65535 || K <= 0 || K % 128 || N <= 0 || N % 128) return -1;
+  if (K > kMaxDepth || M > INT32_MAX || G * N > INT32_MAX) return -1;
   return mx::plan_gemm(M, G, N, K).workspace_bytes;
 }
 
 MX_API int64_t fp8_gemm_nt_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return -1;
+  if (K > kMaxDepth || M > INT32_MAX || N > INT32_MAX) return -1;
   return mx::plan_gemm(M, 1, N, K).workspace_bytes;
 }

@@ -82,6 +82,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f& acc, i
   }
 }
 
+// Workgroup barrier for LDS exchange inside software pipelines: waits for this
+// wave's LDS operations only, then s_barrier.  __syncthreads() would also wait
+// for every global load still in flight (its release fence covers all memory),
+// which would collapse a multi-stage prefetch to a single stage.  The asm is a
+// compiler memory fence as well, so no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Maps a flat workgroup id to a work index so that each XCD (workgroups are
 // dispatched round-robin over the 8 XCDs) receives one contiguous range of work:
 // neighbouring tiles, which share activation rows, then share one L2.

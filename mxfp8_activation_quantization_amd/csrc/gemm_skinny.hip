@@ -2,43 +2,171 @@
 //
 // With at most a few hundred tokens the o_proj chain is bound by reading its
 // weights from HBM once (vLLM PR #60118 "[Perf][DSv4.1] MegaAttn: wo_a writes
-// wo_b's MXFP8 input", Claims: the decode range is 1-256 tokens).  HBM only
-// streams near its peak when every CU keeps many reads in flight, so the work is
-// cut finely: a workgroup owns 64 weight rows (two MFMA row tiles), the tokens of
-// one chunk (32 or 64) and one 1024-deep K slice; wo_a at 64 tokens becomes 512
-// workgroups and wo_b 640.
+// wo_b's MXFP8 input", Claims: the decode range is 1-256 tokens).  HBM streams
+// near its peak only when every CU keeps many reads in flight for the whole
+// kernel, so the grid is sized to be resident in one round (two workgroups per
+// CU) and every workgroup streams a long K range through a software pipeline.
 //
-// Inside a workgroup:
-//   1. each wave issues all loads of its weight fragments at once (4 K-steps of
-//      its 32 rows, straight into registers in the MFMA lane layout);
-//   2. all threads stage the activation slice (tokens x 1024) in LDS with
-//      coalesced 16-byte loads, quantizing BF16 input per 32-block on the way
-//      (four lanes per block, one amax shuffle pair, the standalone quantizer's
-//      rule), so both row tiles read it from LDS;
-//   3. wave (row tile rt, K half kh) runs 4 K-steps of scaled MFMAs;
-//   4. the two K halves are added through LDS (kh 0 + kh 1).
-// With one K slice the workgroup runs the epilogue itself.  Otherwise it writes
-// its fp32 partial tile to the caller's workspace, and the last workgroup of the
-// tile to arrive (an atomic counter) adds the slices in slice order 0, 1, ...,
-// S-1 and runs the epilogue: the result does not depend on arrival order.  The
-// counter is reset to zero for the next call.
+// Work item: 64 weight rows (two MFMA row tiles) x one chunk of up to 64 tokens
+// x one K range (split s of S).  Four waves: wave (rt, tt) owns the 32 x 32
+// output tile of row tile rt and token tile tt.
+//
+// Pipeline: K is walked in super-steps of two 128-deep steps.  All 256 threads
+// load a super-step's weight and activation tiles (64 rows x 256 bytes each,
+// 16 KB + 16 KB, row-contiguous 16-byte loads) into registers; two super-steps
+// are in flight while the MFMAs of a third read LDS.  Registers go to one of two
+// LDS buffers in the fragment-major layout of the LDS-tiled kernel (conflict-free
+// fragment reads), one barrier per super-step.  BF16 activations are quantized on
+// their way into LDS (the four lanes of a 32-block exchange their maxima, the
+// standalone quantizer's rule).
+//
+// Split K: with S > 1 every work item writes its fp32 partial tile to the
+// caller's workspace, and the last of the S items of a tile to arrive (an atomic
+// counter) adds the partials in split order 0, 1, ..., S-1 and runs the
+// epilogue, so the result does not depend on arrival order.  The counter is
+// reset to zero for the next call.
 #include "gemm_common.hpp"
 
 namespace mx {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kSplitSteps = 8;   // 128-K steps per K slice
-constexpr int kHalfSteps = 4;    // steps per wave (two waves per row tile)
+namespace {
 
-__device__ __forceinline__ int sswz(int row, int chunk) { return (row * 8 + (chunk ^ (row & 7))) * 16; }
+constexpr uint32_t kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked
+constexpr int kUncached = 0x11;              // sc0 | sc1: bypass L1 and L2 (partials cross XCDs)
+constexpr int kTileRows = 64;                // weight rows per work item
+constexpr int kChunkTokens = 64;             // tokens per work item (two token tiles)
+constexpr int kStepBytes = 64 * 128;         // one 128-deep step of a 64-row operand tile
+constexpr int kSuper = 2;                    // steps per super-step
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// Fragment-major LDS layout of one 64-row step tile (see gemm_tiled.hip).
+__device__ __forceinline__ int frag_off(int r, int c) {
+  const int T = r >> 5, i = r & 31, KS = c >> 2, h = (c >> 1) & 1, q = c & 1;
+  return (((T * 2 + KS) * 2 + h) * 64 + ((i + 32 * q) ^ (8 * q))) * 16;
+}
+
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int T, int KS, int lane, int q) {
+  const uint8_t* b = tile + ((T * 2 + KS) * 2) * 1024 + (lane ^ (8 * q)) * 16;
+  return frag(*reinterpret_cast<const uint4*>(b), *reinterpret_cast<const uint4*>(b + 1024));
+}
+
+// Registers of one super-step in flight.  Weights and E4M3 activations: thread t
+// of instruction u covers row 8(4u + wave) + (lane & 7), chunk lane >> 3 of step
+// u / 8 (u < 16 over both steps: 64 rows x 8 chunks x 2 steps / 256 threads = 4 per
+// thread per operand).  BF16 activations: 64 rows x 2 steps x 16 chunks / 256 = 8.
+template <bool X_BF16>
+struct Super {
+  uint4 w[4];
+  uint4 x[X_BF16 ? 8 : 4];
+  uint32_t wsf;   // scale word: weight row (tid & 63), step (tid >> 6) & 1
+  uint32_t xsf;   // scale word: token row (tid & 63), step (tid >> 6) & 1 (E4M3 activations)
+};
+
+struct Ctx {
+  __amdgpu_buffer_rsrc_t rw, rws, rx, rxs;
+  int K, ksteps, ld_x_bytes, ld_xsf_bytes, xcol0, xsfcol0;
+  int k_lo, k_hi;         // this item's steps [k_lo, k_hi)
+  int m_rows;             // valid token rows of the chunk; rows past it load row m_rows - 1 and are zeroed
+};
+
+// Step index j of super-step `ss`, clamped into the item's range (loads of a step
+// past the range fetch a valid step; its MFMAs are skipped).
+__device__ __forceinline__ int step_of(const Ctx& c, int ss, int j) {
+  const int k = c.k_lo + ss * kSuper + j;
+  return k < c.k_hi ? k : c.k_hi - 1;
+}
+
+template <bool X_BF16>
+__device__ __forceinline__ void load_super(Super<X_BF16>& st, const Ctx& c, int ss, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
+    st.w[u] = bload16(c.rw, row * c.K + step_of(c, ss, j) * 128 + ch * 16);
+  }
+  {
+    const int row = tid & 63, j = (tid >> 6) & 1;
+    st.wsf = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(c.rws, (row * c.ksteps + step_of(c, ss, j)) * 4, 0, 0);
+  }
+  if constexpr (!X_BF16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
+      const int rc = row < c.m_rows ? row : c.m_rows - 1;
+      const uint4 v = bload16(c.rx, rc * c.ld_x_bytes + c.xcol0 + step_of(c, ss, j) * 128 + ch * 16);
+      st.x[u] = row < c.m_rows ? v : make_uint4(0, 0, 0, 0);
+    }
+    const int row = tid & 63, j = (tid >> 6) & 1, rc = row < c.m_rows ? row : c.m_rows - 1;
+    const uint32_t sv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+        c.rxs, rc * c.ld_xsf_bytes + c.xsfcol0 + step_of(c, ss, j) * 4, 0, 0);
+    st.xsf = row < c.m_rows ? sv : 0u;
+  } else {
+    // instruction u: step u >> 2, rows 16 * ((4 * (u & 3) + wave) >> 2) + (lane & 15), block
+    // (4 * (u & 3) + wave) & 3; lanes l, l+16, l+32, l+48 hold the block's four parts
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = u >> 2, k = 4 * (u & 3) + wave, rg = k >> 2, b = k & 3;
+      const int row = 16 * rg + (lane & 15), jj = 4 * b + (lane >> 4);
+      const int rc = row < c.m_rows ? row : c.m_rows - 1;
+      const uint4 v = bload16(c.rx, rc * c.ld_x_bytes + c.xcol0 + step_of(c, ss, j) * 256 + jj * 16);
+      st.x[u] = row < c.m_rows ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <bool X_BF16>
+__device__ __forceinline__ void store_super(const Super<X_BF16>& st, uint8_t* sW, uint8_t* sX, uint32_t* sWs,
+                                            uint32_t* sXs, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
+    *reinterpret_cast<uint4*>(sW + j * kStepBytes + frag_off(row, ch)) = st.w[u];
+  }
+  sWs[((tid >> 6) & 1) * 64 + (tid & 63)] = st.wsf;   // waves 2, 3 repeat waves 0, 1: same values
+  if constexpr (!X_BF16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
+      *reinterpret_cast<uint4*>(sX + j * kStepBytes + frag_off(row, ch)) = st.x[u];
+    }
+    sXs[((tid >> 6) & 1) * 64 + (tid & 63)] = st.xsf;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = u >> 2, k = 4 * (u & 3) + wave, rg = k >> 2, b = k & 3;
+      const int row = 16 * rg + (lane & 15), part = lane >> 4, jj = 4 * b + part;
+      const uint4 v = st.x[u];
+      uint32_t am = fold_pair(amax_pair(amax_pair(amax_pair(amax_pair(0u, v.x), v.y), v.z), v.w));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      const int e = scale_exp_from_amax(am);
+      const float sc = exp2_int(e);
+      const uint2 codes = make_uint2(encode4(v.x, v.y, sc), encode4(v.z, v.w, sc));
+      *reinterpret_cast<uint2*>(sX + j * kStepBytes + frag_off(row, jj >> 1) + 8 * (jj & 1)) = codes;
+      if (part == 0) reinterpret_cast<uint8_t*>(sXs)[(j * 64 + row) * 4 + b] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+}  // namespace
 
 template <int MT, bool X_BF16, int OUT>
 __global__ __launch_bounds__(kThreads) void splitk_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
-  constexpr int ROWS = 32 * MT;                          // token rows of the chunk
-  constexpr int STEP_BYTES = ROWS * 128;
-  __shared__ __attribute__((aligned(16))) uint8_t sx[kSplitSteps * STEP_BYTES];
-  __shared__ uint32_t sxs[kSplitSteps][ROWS];
+  __shared__ __attribute__((aligned(1024))) uint8_t sW[2][kSuper * kStepBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sX[2][kSuper * kStepBytes];
+  __shared__ uint32_t sWs[2][kSuper * 64];
+  __shared__ uint32_t sXs[2][kSuper * 64];
   __shared__ int s_last;
 
   const int total = G * n_tiles * chunks * S;
@@ -51,145 +179,86 @@ __global__ __launch_bounds__(kThreads) void splitk_kernel(GemmArgs p, int G, int
   const int tc = tile * chunks + chunk;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, q = lane >> 5;
-  const int rt = wave & 1, kh = wave >> 1;
-  const int64_t ksteps = p.K / 128;
-  const int64_t kt0 = (int64_t)s * kSplitSteps;
+  const int rt = wave & 1, tt = wave >> 1;
 
-  // 1. this wave's weight fragments: rows of row tile rt, steps kt0 + 4 kh + j
-  const int64_t n_row = (int64_t)g * p.N + (int64_t)nt * 64 + rt * 32 + i;
-  const uint8_t* wp = p.w + n_row * p.K + 16 * q;
-  const int32_t* wsfp = p.w_sf + n_row * ksteps;
-  uint4 wv[kHalfSteps][4];
-  uint32_t wsw[kHalfSteps];
-#pragma unroll
-  for (int j = 0; j < kHalfSteps; ++j) {
-    const int64_t kt = kt0 + kHalfSteps * kh + j;
-    const int64_t kc = kt < ksteps ? kt : ksteps - 1;     // steps past K: loaded from a valid address, zeroed below
-#pragma unroll
-    for (int c = 0; c < 4; ++c) wv[j][c] = *reinterpret_cast<const uint4*>(wp + kc * 128 + 32 * c);
-    wsw[j] = (uint32_t)wsfp[kc];
-  }
+  Ctx c;
+  c.K = (int)p.K;
+  c.ksteps = (int)(p.K / 128);
+  c.k_lo = (int)((int64_t)s * c.ksteps / S);
+  c.k_hi = (int)((int64_t)(s + 1) * c.ksteps / S);
+  const int nss = (c.k_hi - c.k_lo + kSuper - 1) / kSuper;
+  const int xes = X_BF16 ? 2 : 1;
+  c.ld_x_bytes = (int)(p.ld_x * xes);
+  c.ld_xsf_bytes = (int)(p.ld_xsf * 4);
+  c.xcol0 = (int)((int64_t)g * p.K * xes);
+  c.xsfcol0 = g * c.ksteps * 4;
+  const int64_t n_row0 = (int64_t)g * p.N + (int64_t)nt * kTileRows;
+  const int64_t m_first = (int64_t)chunk * kChunkTokens;
+  const int64_t m_rows = p.M - m_first < kChunkTokens ? p.M - m_first : kChunkTokens;
+  c.m_rows = (int)m_rows;
+  c.rw = make_rsrc(p.w + n_row0 * p.K, (int64_t)kTileRows * p.K);
+  c.rws = make_rsrc(p.w_sf + n_row0 * c.ksteps, (int64_t)kTileRows * c.ksteps * 4);
+  c.rx = make_rsrc(static_cast<const uint8_t*>(p.x) + m_first * c.ld_x_bytes,
+                   (m_rows - 1) * c.ld_x_bytes + (int64_t)G * p.K * xes);
+  c.rxs = X_BF16 ? c.rx
+                 : make_rsrc(p.x_sf + m_first * p.ld_xsf, ((m_rows - 1) * p.ld_xsf + (int64_t)G * c.ksteps) * 4);
 
-  // 2. activation slice -> LDS (E4M3 codes, swizzled 128-byte rows per step, packed scale words)
-  const int64_t m_first = (int64_t)chunk * ROWS;
-  if constexpr (!X_BF16) {
-    const uint8_t* xq = static_cast<const uint8_t*>(p.x);
-#pragma unroll 4
-    for (int c = tid; c < kSplitSteps * ROWS * 8; c += kThreads) {
-      const int j = c / (ROWS * 8), rem = c % (ROWS * 8), row = rem >> 3, ch = rem & 7;
-      const int64_t m = m_first + row < p.M ? m_first + row : p.M - 1;
-      const int64_t kt = kt0 + j;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kt < ksteps) v = *reinterpret_cast<const uint4*>(xq + m * p.ld_x + (int64_t)g * p.K + kt * 128 + ch * 16);
-      *reinterpret_cast<uint4*>(sx + j * STEP_BYTES + sswz(row, ch)) = v;
-    }
-    for (int c = tid; c < kSplitSteps * ROWS; c += kThreads) {
-      const int j = c / ROWS, row = c % ROWS;
-      const int64_t m = m_first + row < p.M ? m_first + row : p.M - 1;
-      const int64_t kt = kt0 + j;
-      sxs[j][row] = kt < ksteps ? (uint32_t)p.x_sf[m * p.ld_xsf + (int64_t)g * ksteps + kt] : 0u;
-    }
-  } else {
-    // BF16: 256 bytes per row and step = 16 lanes x 16 bytes; lanes 4b..4b+3 own 32-block b
-    const uint16_t* xb = static_cast<const uint16_t*>(p.x);
-#pragma unroll 4
-    for (int c = tid; c < kSplitSteps * ROWS * 16; c += kThreads) {
-      const int j = c / (ROWS * 16), rem = c % (ROWS * 16), row = rem >> 4, jj = rem & 15;
-      const int b = jj >> 2, part = jj & 3;
-      const int64_t m = m_first + row < p.M ? m_first + row : p.M - 1;
-      const int64_t kt = kt0 + j;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kt < ksteps) v = *reinterpret_cast<const uint4*>(xb + m * p.ld_x + (int64_t)g * p.K + kt * 128 + jj * 8);
-      uint32_t am = fold_pair(amax_pair(amax_pair(amax_pair(amax_pair(0u, v.x), v.y), v.z), v.w));
-      am = max(am, (uint32_t)__shfl_xor((int)am, 1, 4));
-      am = max(am, (uint32_t)__shfl_xor((int)am, 2, 4));
-      const int e = scale_exp_from_amax(am);
-      const float sc = exp2_int(e);
-      const uint2 codes = make_uint2(encode4(v.x, v.y, sc), encode4(v.z, v.w, sc));
-      *reinterpret_cast<uint2*>(sx + j * STEP_BYTES + sswz(row, 2 * b + (part >> 1)) + (part & 1) * 8) = codes;
-      if (part == 0) reinterpret_cast<uint8_t*>(&sxs[j][row])[b] = (uint8_t)(e + 127);
-    }
-  }
-  __syncthreads();
+  v16f acc = zero16();
+  const bool computes = tt < MT;
 
-  // 3. scaled MFMAs over this wave's four steps
-  v16f acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = zero16();
-#pragma unroll
-  for (int jj = 0; jj < kHalfSteps; ++jj) {
-    const int j = kHalfSteps * kh + jj;
-    const bool valid = kt0 + j < ksteps;
-    uint4 w0 = wv[jj][0], w1 = wv[jj][1], w2 = wv[jj][2], w3 = wv[jj][3];
-    if (!valid) w0 = w1 = w2 = w3 = make_uint4(0, 0, 0, 0);    // exact zero contribution
-    const v8i w01 = frag(w0, w1), w23 = frag(w2, w3);
-    const int sw = (int)(wsw[jj] >> (8 * q));
-    const uint8_t* slab = sx + j * STEP_BYTES;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int row = 32 * t + i;
-      const v8i x01 = frag(*reinterpret_cast<const uint4*>(slab + sswz(row, q)),
-                           *reinterpret_cast<const uint4*>(slab + sswz(row, 2 + q)));
-      const v8i x23 = frag(*reinterpret_cast<const uint4*>(slab + sswz(row, 4 + q)),
-                           *reinterpret_cast<const uint4*>(slab + sswz(row, 6 + q)));
-      const int sxw = (int)(sxs[j][row] >> (8 * q));
-      acc[t] = mfma_scaled<0>(w01, x01, acc[t], sw, sxw);
-      acc[t] = mfma_scaled<2>(w23, x23, acc[t], sw, sxw);
-    }
-  }
+  Super<X_BF16> st0, st1;
+  load_super<X_BF16>(st0, c, 0, tid);
+  if (nss > 1) load_super<X_BF16>(st1, c, 1, tid);
 
-  // 4. K halves: kh 0 + kh 1, through LDS (the activation slice is no longer needed)
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(sx);           // [rt][t][16][64]
-  if (kh == 1) {
+  // One super-step: the older registers in flight go to LDS buffer b, the next
+  // loads reuse them, and the MFMAs read buffer b.
+  auto body = [&](Super<X_BF16>& st, int ss, int b) {
+    store_super<X_BF16>(st, sW[b], sX[b], sWs[b], sXs[b], tid);
+    lds_barrier();
+    if (ss + 2 < nss) load_super<X_BF16>(st, c, ss + 2, tid);
+    if (computes) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[((rt * MT + t) * 16 + r) * 64 + lane] = acc[t][r];
-  }
-  __syncthreads();
-  if (kh == 0) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] += red[((rt * MT + t) * 16 + r) * 64 + lane];
-  }
-
-  const int64_t nb = (int64_t)g * p.N + (int64_t)nt * 64 + rt * 32;
-  if (S == 1) {
-    if (kh == 0) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int64_t m = m_first + 32 * t + i;
-        store_tile<OUT>(p, acc[t], m, m < p.M, nb, q);
+      for (int j = 0; j < kSuper; ++j) {
+        if (c.k_lo + ss * kSuper + j < c.k_hi) {
+          const uint8_t* tw = sW[b] + j * kStepBytes;
+          const uint8_t* tx = sX[b] + j * kStepBytes;
+          const int sw = (int)(sWs[b][j * 64 + rt * 32 + i] >> (8 * q));
+          const int sx = (int)(sXs[b][j * 64 + tt * 32 + i] >> (8 * q));
+          acc = mfma_scaled<0>(read_frag(tw, rt, 0, lane, q), read_frag(tx, tt, 0, lane, q), acc, sw, sx);
+          acc = mfma_scaled<2>(read_frag(tw, rt, 1, lane, q), read_frag(tx, tt, 1, lane, q), acc, sw, sx);
+        }
       }
     }
+  };
+  for (int ss = 0; ss < nss; ss += 2) {
+    body(st0, ss, 0);
+    if (ss + 1 < nss) body(st1, ss + 1, 1);
+  }
+
+  const int64_t nb = n_row0 + rt * 32;
+  const int64_t m = m_first + tt * 32 + i;
+  if (S == 1) {
+    if (computes) store_tile<OUT>(p, acc, m, m < p.M, nb, q);
     return;
   }
 
-  // 5. split K: publish the partial tile; the last slice to arrive reduces in slice order.
-  // The slices of a tile may run on different XCDs, whose L2 caches are not
-  // coherent with each other.  Partial tiles therefore move with 16-byte buffer
-  // accesses that bypass L1 and L2 (sc0 sc1), and the counter with a relaxed
-  // system-scope atomic: a writer waits until its stores are complete before it
-  // bumps the counter, and the last workgroup reads the partials from memory.  No
-  // cache-wide writeback or invalidate is needed, so other workgroups keep their
-  // cached activations.  Partial layout per slice: [rt][t][lane][16 floats].
+  // Split K: publish this item's partial tile.  The items of a tile may run on
+  // different XCDs, whose L2 caches are not coherent with each other, so partials
+  // move with 16-byte buffer accesses that bypass L1 and L2 (sc0 sc1), and the
+  // counter with a relaxed system-scope atomic: a writer waits until its stores
+  // are complete before it bumps the counter, and the last one reads the partials
+  // from memory.  Partial layout per split: [rt][tt][lane][16 floats].
   constexpr int TILE_FLOATS = 2 * MT * 16 * 64;
   constexpr int TILE_BYTES = TILE_FLOATS * 4;
-  constexpr int kUncached = 0x11;                           // sc0 | sc1
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      p.ws_partials + (int64_t)tc * S * TILE_FLOATS, 0, S * TILE_BYTES, 0x00020000);
-  if (kh == 0) {
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_partials + (int64_t)tc * S * TILE_FLOATS, 0, S * TILE_BYTES, kRsrcFlags);
+  const int my_off = ((rt * MT + tt) * 64 + lane) * 64;     // bytes within a split's tile
+  if (computes) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int base = s * TILE_BYTES + ((rt * MT + t) * 64 + lane) * 64;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const v4i v = {__float_as_int(acc[t][4 * k]), __float_as_int(acc[t][4 * k + 1]),
-                       __float_as_int(acc[t][4 * k + 2]), __float_as_int(acc[t][4 * k + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, base + 16 * k, 0, kUncached);
-      }
+    for (int k = 0; k < 4; ++k) {
+      const v4i v = {__float_as_int(acc[4 * k]), __float_as_int(acc[4 * k + 1]), __float_as_int(acc[4 * k + 2]),
+                     __float_as_int(acc[4 * k + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rp, s * TILE_BYTES + my_off + 16 * k, 0, kUncached);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -198,54 +267,33 @@ __global__ __launch_bounds__(kThreads) void splitk_kernel(GemmArgs p, int G, int
     s_last = __hip_atomic_fetch_add(&p.ws_counters[tc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
              (uint32_t)(S - 1);
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last || !computes) return;
 
-  // every thread sums its 16-byte chunks of the tile over the slices, in slice order
-  constexpr int CH = TILE_BYTES / 16 / kThreads;            // chunks per thread (2 MT)
-  float4 sum[CH];
+  // the last item: each wave sums its own 32 x 32 tile over the splits, in split order
+  v16f tot = zero16();
+  for (int s0 = 0; s0 < S; s0 += 2) {
+    v4i ld[2][4];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) sum[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S; s0 += 4) {
-    v4i ld[4][CH];
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int k = 0; k < 4; ++k)
+        ld[u][k] = s0 + u < S ? __builtin_amdgcn_raw_buffer_load_b128(rp, (s0 + u) * TILE_BYTES + my_off + 16 * k, 0,
+                                                                      kUncached)
+                              : v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (s0 + u < S)
-          ld[u][c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (s0 + u) * TILE_BYTES + (c * kThreads + tid) * 16,
-                                                           0, kUncached);
+    for (int u = 0; u < 2; ++u) {
+      if (s0 + u < S) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (s0 + u < S) {
-          if (s0 + u == 0) {
-            sum[c] = make_float4(__int_as_float(ld[u][c].x), __int_as_float(ld[u][c].y),
-                                 __int_as_float(ld[u][c].z), __int_as_float(ld[u][c].w));
-          } else {
-            sum[c].x += __int_as_float(ld[u][c].x);
-            sum[c].y += __int_as_float(ld[u][c].y);
-            sum[c].z += __int_as_float(ld[u][c].z);
-            sum[c].w += __int_as_float(ld[u][c].w);
-          }
+        for (int k = 0; k < 4; ++k) {
+          tot[4 * k] += __int_as_float(ld[u][k].x);
+          tot[4 * k + 1] += __int_as_float(ld[u][k].y);
+          tot[4 * k + 2] += __int_as_float(ld[u][k].z);
+          tot[4 * k + 3] += __int_as_float(ld[u][k].w);
         }
-  }
-  // back to the MFMA lane layout through LDS, then the epilogue
-  float4* red4 = reinterpret_cast<float4*>(sx);
-#pragma unroll
-  for (int c = 0; c < CH; ++c) red4[c * kThreads + tid] = sum[c];
-  __syncthreads();
-  if (kh == 0) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const float* src = reinterpret_cast<const float*>(sx) + ((rt * MT + t) * 64 + lane) * 16;
-      v16f tot;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tot[r] = src[r];
-      const int64_t m = m_first + 32 * t + i;
-      store_tile<OUT>(p, tot, m, m < p.M, nb, q);
+      }
     }
   }
+  store_tile<OUT>(p, tot, m, m < p.M, nb, q);
   if (tid == 0) __hip_atomic_store(&p.ws_counters[tc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 

@@ -1,5 +1,5 @@
-// Block-scaled FP8 GEMM, LDS-tiled variant for many tokens, on gfx950's
-// V_MFMA_SCALE_F32_32X32X64_F8F6F4.
+// Block-scaled FP8 GEMM for many tokens (prefill): LDS-tiled, double-buffered,
+// on gfx950's V_MFMA_SCALE_F32_32X32X64_F8F6F4.
 //
 // One kernel family serves both projections of the o_proj chain:
 //   * grouped_fp8_einsum (wo_a): G groups, z[m, g*N+n] = sum_k x[m, g*K+k] w[g,n,k],
@@ -11,186 +11,522 @@
 // which the load path quantizes with the same rule as mxfp8_quantize (PR #57977,
 // Test Result: pre-quantized input is bit-identical to in-kernel quantization).
 //
-// MFMA roles and lane layout: see gemm_common.hpp.
+// Tiling.  A workgroup of four waves owns BN weight rows x BM tokens and walks K
+// in steps of 128 bytes (exactly one packed scale word per row and step).  Wave
+// (wn, wm) owns a (BN / WAVES_N) x (BM / WAVES_M) sub-tile of 32 x 32 MFMA tiles,
+// so one step is 2 * TN * TM scaled MFMAs per wave.  Both operand tiles of a step
+// live in LDS, twice (double buffer): while the MFMAs of step k read one buffer,
+// the loads of step k+1 are in flight into registers and are written into the
+// other buffer afterwards, so one barrier per step suffices.
 //
-// Tiles: a block owns BN weight rows x BM tokens and walks K in steps of 128
-// (exactly one packed scale word per row).  Both operand tiles are staged in
-// LDS, 128 bytes per row with the 16-byte chunks XOR-swizzled by row to spread
-// the MFMA fragment reads over the banks; the scale words are staged beside them.
+// LDS layout ("fragment-major").  An MFMA operand fragment is the 32 bytes lane
+// l = i + 32q needs for one 64-deep half KS of a step: chunks 4KS + q and
+// 4KS + 2 + q (16 bytes each) of tile row 32T + i.  Chunk c of row r is stored at
+//     16 * (64 * ((2T + KS) * 2 + h) + ((i + 32q) ^ 8q)),  KS = c/4, h = (c/2)%2, q = c%2,
+// so a wave reads one fragment half with one ds_read_b128 over 64 consecutive
+// 16-byte slots (bank-conflict free), and the 8 rows x 8 chunks one global-load
+// instruction brings in land in distinct bank groups when written.
+//
+// Token rows past M: the register-staged kernel loads a valid row instead and
+// zeroes the value (code 0; BF16 zero quantizes to code 0 with scale byte 0); the
+// direct-to-LDS kernel keeps the row part of every offset in the per-lane
+// register, which the buffer range check covers (the scalar offset is not
+// checked), and sets the range to end at row M, so those rows arrive as zeros.
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace mx {
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (row * 8 + (chunk ^ (row & 7))) * 16; }
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-// The 32-byte fragment of LDS tile row `row` for 64-deep half KS and lane half q.
-template <int KS>
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int q) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + swz(row, 4 * KS + q));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + swz(row, 4 * KS + 2 + q));
-  return frag(lo, hi);
+constexpr uint32_t kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
 }
 
-template <int BN_, int BM_, int WN_, int WM_>
-struct TileCfg {
-  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Byte offset of 16-byte chunk c (0..7) of tile row r in the fragment-major layout.
+__device__ __forceinline__ int frag_off(int r, int c) {
+  const int T = r >> 5, i = r & 31, KS = c >> 2, h = (c >> 1) & 1, q = c & 1;
+  return (((T * 2 + KS) * 2 + h) * 64 + ((i + 32 * q) ^ (8 * q))) * 16;
+}
+
+// The fragment of MFMA row tile T, 64-deep half KS, for lane l (q = l / 32).
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int T, int KS, int lane, int q) {
+  const int slot = lane ^ (8 * q);
+  const uint8_t* b = tile + ((T * 2 + KS) * 2) * 1024 + slot * 16;
+  return frag(*reinterpret_cast<const uint4*>(b), *reinterpret_cast<const uint4*>(b + 1024));
+}
+
+template <int BN_, int BM_, int WAVES_N_, int WAVES_M_>
+struct BigCfg {
+  static constexpr int BN = BN_, BM = BM_, WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
+  static constexpr int NW = WAVES_N * WAVES_M, THREADS = 64 * NW;
+  static constexpr int WN = BN / WAVES_N, WM = BM / WAVES_M;
   static constexpr int TN = WN / 32, TM = WM / 32;
-  static constexpr int WAVES_N = BN / WN, WAVES_M = BM / WM;
-  static_assert(WAVES_N * WAVES_M == 4, "four waves per block");
-  static_assert(BN % 32 == 0 && BM % 32 == 0, "32-row MFMA tiles");
+  static_assert(WN % 32 == 0 && WM % 32 == 0, "32-row MFMA tiles");
+  static constexpr int W_LOADS = BN * 8 / THREADS;       // 16-byte weight chunks per thread and step
+  static constexpr int XQ_LOADS = BM * 8 / THREADS;      // 16-byte E4M3 activation chunks
+  static constexpr int XB_LOADS = BM * 16 / THREADS;     // 16-byte BF16 activation chunks
+  static_assert(W_LOADS * THREADS == BN * 8 && XQ_LOADS * THREADS == BM * 8 && XB_LOADS * THREADS == BM * 16,
+                "load mapping");
+  static_assert(THREADS % BN == 0 && THREADS % BM == 0, "scale words: every row covered by a thread");
 };
 
+template <class C, bool X_BF16>
+struct Stage {
+  uint4 w[C::W_LOADS];
+  uint4 x[X_BF16 ? C::XB_LOADS : C::XQ_LOADS];
+  uint32_t wsf;   // scale word of weight row tid % BN
+  uint32_t xsf;   // scale word of token row tid % BM (E4M3 activations)
+};
+
+template <class C, bool X_BF16>
+__device__ __forceinline__ void load_stage(Stage<C, X_BF16>& st, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rws,
+                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rxs, int64_t K,
+                                           int ksteps, int ld_x_bytes, int ld_xsf_bytes, int xcol0, int xsfcol0,
+                                           int kt, int tid, int m_rows) {
+  const int wave = tid >> 6, lane = tid & 63;
+  // weights: instruction u of wave w covers rows 8(4u + w) .. +7, all 8 chunks of the step
+#pragma unroll
+  for (int u = 0; u < C::W_LOADS; ++u) {
+    const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
+    st.w[u] = bload16(rw, row * (int)K + kt * 128 + c * 16);
+  }
+  st.wsf = bload4(rws, ((tid % C::BN) * ksteps + kt) * 4);
+  if constexpr (!X_BF16) {
+#pragma unroll
+    for (int u = 0; u < C::XQ_LOADS; ++u) {
+      const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
+      const int rc = row < m_rows ? row : m_rows - 1;
+      const uint4 v = bload16(rx, rc * ld_x_bytes + xcol0 + kt * 128 + c * 16);
+      st.x[u] = row < m_rows ? v : make_uint4(0, 0, 0, 0);
+    }
+    const int srow = tid % C::BM, src = srow < m_rows ? srow : m_rows - 1;
+    const uint32_t sv = bload4(rxs, src * ld_xsf_bytes + xsfcol0 + kt * 4);
+    st.xsf = srow < m_rows ? sv : 0u;
+  } else {
+    // BF16: instruction u covers 16 rows x one 32-element block b; the four lanes
+    // l, l+16, l+32, l+48 hold the block's four 16-byte parts.
+#pragma unroll
+    for (int u = 0; u < C::XB_LOADS; ++u) {
+      const int k = C::NW * u + wave, rg = k >> 2, b = k & 3;
+      const int row = 16 * rg + (lane & 15), jj = 4 * b + (lane >> 4);
+      const int rc = row < m_rows ? row : m_rows - 1;
+      const uint4 v = bload16(rx, rc * ld_x_bytes + xcol0 + kt * 256 + jj * 16);
+      st.x[u] = row < m_rows ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <class C, bool X_BF16>
+__device__ __forceinline__ void store_stage(const Stage<C, X_BF16>& st, uint8_t* sW, uint8_t* sX, uint32_t* sWs,
+                                            uint32_t* sXs, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int u = 0; u < C::W_LOADS; ++u) {
+    const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
+    *reinterpret_cast<uint4*>(sW + frag_off(row, c)) = st.w[u];
+  }
+  sWs[tid % C::BN] = st.wsf;        // threads past BN repeat a row's word: same value, same slot
+  if constexpr (!X_BF16) {
+#pragma unroll
+    for (int u = 0; u < C::XQ_LOADS; ++u) {
+      const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
+      *reinterpret_cast<uint4*>(sX + frag_off(row, c)) = st.x[u];
+    }
+    sXs[tid % C::BM] = st.xsf;
+  } else {
+#pragma unroll
+    for (int u = 0; u < C::XB_LOADS; ++u) {
+      const int k = C::NW * u + wave, rg = k >> 2, b = k & 3;
+      const int row = 16 * rg + (lane & 15), part = lane >> 4, jj = 4 * b + part;
+      const uint4 v = st.x[u];
+      uint32_t am = fold_pair(amax_pair(amax_pair(amax_pair(amax_pair(0u, v.x), v.y), v.z), v.w));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      const int e = scale_exp_from_amax(am);
+      const float sc = exp2_int(e);
+      const uint2 codes = make_uint2(encode4(v.x, v.y, sc), encode4(v.z, v.w, sc));
+      *reinterpret_cast<uint2*>(sX + frag_off(row, jj >> 1) + 8 * (jj & 1)) = codes;
+      if (part == 0) reinterpret_cast<uint8_t*>(sXs)[row * 4 + b] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// One 128-deep step of a wave's sub-tile: two 64-deep halves of TN x TM scaled MFMAs.
+template <class C>
+__device__ __forceinline__ void mma_step(v16f (&acc)[C::TN][C::TM], const uint8_t* sW, const uint8_t* sX,
+                                         const uint32_t* sWs, const uint32_t* sXs, int wn, int wm, int lane, int q,
+                                         int i) {
+  int sw[C::TN], sx[C::TM];
+#pragma unroll
+  for (int a = 0; a < C::TN; ++a) sw[a] = (int)(sWs[(wn * C::TN + a) * 32 + i] >> (8 * q));
+#pragma unroll
+  for (int b = 0; b < C::TM; ++b) sx[b] = (int)(sXs[(wm * C::TM + b) * 32 + i] >> (8 * q));
+  {
+    v8i fw[C::TN], fx[C::TM];
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a) fw[a] = read_frag(sW, wn * C::TN + a, 0, lane, q);
+#pragma unroll
+    for (int b = 0; b < C::TM; ++b) fx[b] = read_frag(sX, wm * C::TM + b, 0, lane, q);
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<0>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
+  }
+#ifdef MX_KS_BARRIER
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+  {
+    v8i fw[C::TN], fx[C::TM];
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a) fw[a] = read_frag(sW, wn * C::TN + a, 1, lane, q);
+#pragma unroll
+    for (int b = 0; b < C::TM; ++b) fx[b] = read_frag(sX, wm * C::TM + b, 1, lane, q);
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
+  }
+}
+
 template <class C, bool X_BF16, int OUT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sW[C::BN * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t sX[C::BM * 128];
-  __shared__ uint32_t sWs[C::BN];
-  __shared__ uint32_t sXs[C::BM];
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
+void big_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sW[2][C::BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sX[2][C::BM * 128];
+  __shared__ uint32_t sWs[2][C::BN];
+  __shared__ uint32_t sXs[2][C::BM];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 5, i = lane & 31;
   const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
-  const int i = lane & 31, q = lane >> 5;
 
-  const int64_t g = blockIdx.z;
-  const int64_t n0 = (int64_t)blockIdx.x * C::BN;         // within the group
-  const int64_t m0 = (int64_t)blockIdx.y * C::BM;
-  const int64_t ksteps = p.K / 128;
+  const int total = G * m_tiles * n_tiles;
+  const int wi = xcd_work_index((int)blockIdx.x, total);
+  const int nt = wi % n_tiles;
+  const int rest = wi / n_tiles;
+  const int mt = rest % m_tiles;
+  const int g = rest / m_tiles;
 
-  const uint8_t* wbase = p.w + (g * p.N + n0) * p.K;
-  const int32_t* wsf = p.w_sf + (g * p.N + n0) * ksteps;
+  const int64_t n0 = (int64_t)nt * C::BN;                 // within the group
+  const int64_t m0 = (int64_t)mt * C::BM;
+  const int ksteps = (int)(p.K / 128);
+  const int64_t rows_left = p.M - m0;
+  const int64_t m_rows = rows_left < C::BM ? rows_left : C::BM;
+
+  const int xes = X_BF16 ? 2 : 1;
+  const int ld_x_bytes = (int)(p.ld_x * xes);
+  const int ld_xsf_bytes = (int)(p.ld_xsf * 4);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + ((int64_t)g * p.N + n0) * p.K, (int64_t)C::BN * p.K);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_sf + ((int64_t)g * p.N + n0) * ksteps, (int64_t)C::BN * ksteps * 4);
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(static_cast<const uint8_t*>(p.x) + m0 * ld_x_bytes, (m_rows - 1) * ld_x_bytes + p.K * G * xes);
+  const __amdgpu_buffer_rsrc_t rxs =
+      X_BF16 ? rx : make_rsrc(p.x_sf + m0 * p.ld_xsf, ((m_rows - 1) * p.ld_xsf + G * ksteps) * 4);
+  const int xcol0 = (int)((int64_t)g * p.K * xes);
+  const int xsfcol0 = g * ksteps * 4;
 
   v16f acc[C::TN][C::TM];
 #pragma unroll
   for (int a = 0; a < C::TN; ++a)
 #pragma unroll
-    for (int b = 0; b < C::TM; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    for (int b = 0; b < C::TM; ++b) acc[a][b] = zero16();
 
-  for (int64_t kt = 0; kt < ksteps; ++kt) {
-    // ---- stage the weight tile: BN rows x 128 bytes, 16 bytes per thread-iteration
-#pragma unroll
-    for (int c = tid; c < C::BN * 8; c += kThreads) {
-      const int row = c >> 3, ch = c & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(wbase + (int64_t)row * p.K + kt * 128 + ch * 16);
-      *reinterpret_cast<uint4*>(sW + swz(row, ch)) = v;
-    }
-    for (int r = tid; r < C::BN; r += kThreads) sWs[r] = (uint32_t)wsf[(int64_t)r * ksteps + kt];
+  Stage<C, X_BF16> st;
+  load_stage<C, X_BF16>(st, rw, rws, rx, rxs, p.K, ksteps, ld_x_bytes, ld_xsf_bytes, xcol0, xsfcol0, 0, tid, (int)m_rows);
+  store_stage<C, X_BF16>(st, sW[0], sX[0], sWs[0], sXs[0], tid);
+  lds_barrier();
 
-    // ---- stage the activation tile
-    if constexpr (!X_BF16) {
-      const uint8_t* xq = static_cast<const uint8_t*>(p.x);
-#pragma unroll
-      for (int c = tid; c < C::BM * 8; c += kThreads) {
-        const int row = c >> 3, ch = c & 7;
-        const int64_t m = m0 + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (m < p.M) v = *reinterpret_cast<const uint4*>(xq + m * p.ld_x + g * p.K + kt * 128 + ch * 16);
-        *reinterpret_cast<uint4*>(sX + swz(row, ch)) = v;
-      }
-      for (int r = tid; r < C::BM; r += kThreads) {
-        const int64_t m = m0 + r;
-        sXs[r] = m < p.M ? (uint32_t)p.x_sf[m * p.ld_xsf + g * ksteps + kt] : 0u;
-      }
-    } else {
-      // BF16 rows: 256 bytes per row = 16 lanes x 16 bytes; the lane quad 4b..4b+3 of a
-      // row owns 32-element block b and quantizes it like mxfp8_quantize does.
-      const uint16_t* xb = static_cast<const uint16_t*>(p.x);
-#pragma unroll
-      for (int c = tid; c < C::BM * 16; c += kThreads) {
-        const int row = c >> 4, jj = c & 15, b = jj >> 2, part = jj & 3;
-        const int64_t m = m0 + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (m < p.M) v = *reinterpret_cast<const uint4*>(xb + m * p.ld_x + g * p.K + kt * 128 + jj * 8);
-        uint32_t am = fold_pair(amax_pair(amax_pair(amax_pair(amax_pair(0u, v.x), v.y), v.z), v.w));
-        am = max(am, (uint32_t)__shfl_xor((int)am, 1, 4));
-        am = max(am, (uint32_t)__shfl_xor((int)am, 2, 4));
-        const int e = scale_exp_from_amax(am);
-        const float scale = exp2_int(e);
-        const uint2 codes = make_uint2(encode4(v.x, v.y, scale), encode4(v.z, v.w, scale));
-        const int ch = 2 * b + (part >> 1);
-        *reinterpret_cast<uint2*>(sX + swz(row, ch) + (part & 1) * 8) = codes;
-        if (part == 0) reinterpret_cast<uint8_t*>(sXs)[row * 4 + b] = (uint8_t)(e + 127);
-      }
-    }
-    __syncthreads();
-
-    // ---- MFMA over the two 64-deep halves of the step
-    {
-      v8i fw[C::TN], fx[C::TM];
-      int sw[C::TN], sx[C::TM];
-#pragma unroll
-      for (int a = 0; a < C::TN; ++a) {
-        const int row = wn * C::WN + a * 32 + i;
-        fw[a] = read_frag<0>(sW, row, q);
-        sw[a] = (int)(sWs[row] >> (8 * q));
-      }
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b) {
-        const int row = wm * C::WM + b * 32 + i;
-        fx[b] = read_frag<0>(sX, row, q);
-        sx[b] = (int)(sXs[row] >> (8 * q));
-      }
-#pragma unroll
-      for (int a = 0; a < C::TN; ++a)
-#pragma unroll
-        for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<0>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
-#pragma unroll
-      for (int a = 0; a < C::TN; ++a) fw[a] = read_frag<1>(sW, wn * C::WN + a * 32 + i, q);
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b) fx[b] = read_frag<1>(sX, wm * C::WM + b * 32 + i, q);
-#pragma unroll
-      for (int a = 0; a < C::TN; ++a)
-#pragma unroll
-        for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
-    }
-    __syncthreads();
+  // Steps 0 .. ksteps-2 prefetch the next step; the last step is peeled off.
+  for (int kt = 0; kt + 1 < ksteps; ++kt) {
+    const int s = kt & 1;
+    load_stage<C, X_BF16>(st, rw, rws, rx, rxs, p.K, ksteps, ld_x_bytes, ld_xsf_bytes, xcol0, xsfcol0, kt + 1, tid, (int)m_rows);
+    // keep the order: loads in flight across the MFMAs, LDS stores after them
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step<C>(acc, sW[s], sX[s], sWs[s], sXs[s], wn, wm, lane, q, i);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage<C, X_BF16>(st, sW[s ^ 1], sX[s ^ 1], sWs[s ^ 1], sXs[s ^ 1], tid);
+    lds_barrier();
+  }
+  {
+    const int s = (ksteps - 1) & 1;
+    mma_step<C>(acc, sW[s], sX[s], sWs[s], sXs[s], wn, wm, lane, q, i);
   }
 
   // ---- epilogue
 #pragma unroll
   for (int b = 0; b < C::TM; ++b) {
-    const int64_t m = m0 + wm * C::WM + b * 32 + i;
+    const int64_t m = m0 + (wm * C::TM + b) * 32 + i;
 #pragma unroll
     for (int a = 0; a < C::TN; ++a)
-      store_tile<OUT>(p, acc[a][b], m, m < p.M, g * p.N + n0 + wn * C::WN + a * 32, q);
+      store_tile<OUT>(p, acc[a][b], m, m < p.M, (int64_t)g * p.N + n0 + (wn * C::TN + a) * 32, q);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 activations: direct-to-LDS variant.
+//
+// Both operands are already codes, so they go from memory straight into LDS
+// (buffer_load_dwordx4 ... lds: lane l of an instruction writes 16 bytes at
+// LDS base + 16 l) and no registers stage them.  That frees enough LDS to keep
+// four half-step stages (64-deep: 256 rows x 64 bytes per operand = 16 KB), so
+// the loads of stage t+3 are issued while stage t is multiplied -- three stages
+// of latency cover instead of one.
+//
+// Stage layout of one operand: row tile T (32 rows) is a 2 KB block of 128
+// 16-byte slots; chunk cc (0..3, = 2h + q) of row r sits in slot
+//     4r + (cc ^ g(r)),   g(r) = ((r >> 1) ^ (r >> 3)) & 1 | ((r >> 2) & 1) << 1,
+// so one load instruction (64 lanes = 16 rows x 4 chunks, row-contiguous 64 bytes
+// each) fills 1 KB of consecutive slots, and the 16 lanes of one fragment read
+// (16 rows, one chunk) hit 16 different 16-byte bank groups (8 for any 8 rows).
+// The fragment of lane (i, q) is chunk q (dwords 0-3) and chunk 2 + q (dwords
+// 4-7) of row i: the same operand bytes, in the same MFMA order, as the
+// register-staged kernel above, so both kernels give identical bits.
+__device__ __forceinline__ int dl_g(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
+
+__device__ __forceinline__ v8i dl_read_frag(const uint8_t* stage_op, int T, int lane) {
+  const int i = lane & 31, q = lane >> 5, gi = dl_g(i);
+  const uint8_t* b = stage_op + T * 2048 + 64 * i;
+  return frag(*reinterpret_cast<const uint4*>(b + 16 * (q ^ gi)), *reinterpret_cast<const uint4*>(b + 16 * ((2 + q) ^ gi)));
+}
+
+// Direct-to-LDS loads are written as inline assembly on purpose: the compiler
+// tracks its own LDS-DMA builtins conservatively and would wait for every one in
+// flight before each LDS read, which would undo the pipeline.  The kernel does
+// its own counting (s_waitcnt vmcnt) and its own barriers.  The buffer resource
+// is built by hand: base address, stride 0, byte range, raw-buffer flags.
+struct Rsrc {
+  v4i v;
+};
+
+__device__ __forceinline__ Rsrc make_rsrc_sgpr(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  Rsrc r;
+  r.v = v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)kRsrcFlags};
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// 64 lanes x 16 bytes from rsrc + voff + soff into LDS [lds, lds + 1024), lane l at lds + 16 l.
+__device__ __forceinline__ void dl_load16(const Rsrc& r, const void* lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
+}
+
+// 64 lanes x 4 bytes, lane l at lds + 4 l.
+__device__ __forceinline__ void dl_load4(const Rsrc& r, const void* lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
+}
+
+template <class C>
+struct DlStage {
+  uint8_t w[C::BN * 64];
+  uint8_t x[C::BM * 64];
+  uint32_t ws[C::BN];
+  uint32_t xs[C::BM];
+};
+
+template <class C, int OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
+  static_assert(C::NW == 4, "four waves");
+  constexpr int WI = C::BN / 64;                 // weight load instructions per wave and stage
+  constexpr int XI = C::BM / 64;                 // activation load instructions per wave and stage
+  constexpr int L = WI + XI + 2;                 // + one scale-word load per operand
+  // four separate stage buffers: the compiler can then tell a stage being filled
+  // from the stage being read and inserts no waits of its own between them
+  __shared__ __attribute__((aligned(1024))) DlStage<C> st0, st1, st2, st3;
+
+  // the wave index is uniform: keep it in a scalar register (load offsets and LDS bases derive from it)
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 5, i = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
+
+  const int total = G * m_tiles * n_tiles;
+  const int wi = xcd_work_index((int)blockIdx.x, total);
+  const int nt = wi % n_tiles;
+  const int rest = wi / n_tiles;
+  const int mt = rest % m_tiles;
+  const int g = rest / m_tiles;
+
+  const int64_t n0 = (int64_t)nt * C::BN;
+  const int64_t m0 = (int64_t)mt * C::BM;
+  const int ksteps = (int)(p.K / 128);
+  const int nst = 2 * ksteps;
+  const int64_t rows_left = p.M - m0;
+  const int64_t m_rows = rows_left < C::BM ? rows_left : C::BM;
+  const int ldw = (int)p.K, ldx = (int)p.ld_x, ldxs = (int)(p.ld_xsf * 4);
+  const Rsrc rw = make_rsrc_sgpr(p.w + ((int64_t)g * p.N + n0) * p.K, (int64_t)C::BN * p.K);
+  const Rsrc rws = make_rsrc_sgpr(p.w_sf + ((int64_t)g * p.N + n0) * ksteps, (int64_t)C::BN * ksteps * 4);
+  // activation ranges end at token row m_rows (row starts only: see the offsets below)
+  const Rsrc rx = make_rsrc_sgpr(static_cast<const uint8_t*>(p.x) + m0 * ldx, m_rows * ldx);
+  const Rsrc rxs = make_rsrc_sgpr(p.x_sf + m0 * p.ld_xsf, m_rows * ldxs);
+  const int xcol0 = (int)((int64_t)g * p.K);
+  const int xsfcol0 = g * ksteps * 4;
+
+  // Per-lane parts of the load offsets.  Activation offsets carry the whole row
+  // part (row * ld) in the per-lane register -- the only part the range check
+  // sees -- and the column part (< ld) in the scalar offset, so a row at or past
+  // m_rows is out of range and loads zeros.
+  const int lr = lane >> 2, lc = (lane & 3) ^ dl_g(lane >> 2);
+  const int vw = lr * ldw + lc * 16;
+  const int vws = lane * ksteps * 4;
+  int vx[XI];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) vx[j] = (16 * (4 * j + wave) + lr) * ldx + lc * 16;
+  const int vxs = (64 * (wave % (C::BM / 64)) + lane) * ldxs;
+
+  auto issue = [&](DlStage<C>& S, int t) {
+    const int kt = t >> 1, ks = t & 1;
+#pragma unroll
+    for (int j = 0; j < WI; ++j) {
+      const int n = 4 * j + wave;                 // rows 16n .. 16n+15
+      dl_load16(rw, S.w + n * 1024, vw, 16 * n * ldw + kt * 128 + ks * 64);
+    }
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+      const int n = 4 * j + wave;
+      dl_load16(rx, S.x + n * 1024, vx[j], xcol0 + kt * 128 + ks * 64);
+    }
+    const int jw = wave % (C::BN / 64), jx = wave % (C::BM / 64);
+    dl_load4(rws, S.ws + 64 * jw, vws, (64 * jw * ksteps + kt) * 4);
+    dl_load4(rxs, S.xs + 64 * jx, vxs, xsfcol0 + kt * 4);
+  };
+
+  v16f acc[C::TN][C::TM];
+#pragma unroll
+  for (int a = 0; a < C::TN; ++a)
+#pragma unroll
+    for (int b = 0; b < C::TM; ++b) acc[a][b] = zero16();
+
+  auto compute = [&](const DlStage<C>& S, auto ks_tag) {
+    constexpr int KS = decltype(ks_tag)::value;
+    int sw[C::TN], sx[C::TM];
+    v8i fw[C::TN], fx[C::TM];
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a) {
+      sw[a] = (int)(S.ws[(wn * C::TN + a) * 32 + i] >> (8 * q));
+      fw[a] = dl_read_frag(S.w, wn * C::TN + a, lane);
+    }
+#pragma unroll
+    for (int b = 0; b < C::TM; ++b) {
+      sx[b] = (int)(S.xs[(wm * C::TM + b) * 32 + i] >> (8 * q));
+      fx[b] = dl_read_frag(S.x, wm * C::TM + b, lane);
+    }
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2 * KS>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
+  };
+
+  // Stage t lives in buffer t % 4.  Before stage t is read: this wave's loads of
+  // stage t are complete (at most the stages after it, up to t+2, still in
+  // flight: L loads each), then a barrier makes every wave's loads visible and
+  // guarantees that stage t-1's buffer is no longer read, so stage t+3 can be
+  // issued into it.
+  auto step = [&](DlStage<C>& cur, DlStage<C>& nxt3, int t, auto ks_tag) {
+    if (t + 2 < nst) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
+    else if (t + 1 < nst) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");   // no LDS writes of its own: vmcnt above covers the DMA
+    if (t + 3 < nst) issue(nxt3, t + 3);
+    compute(cur, ks_tag);
+  };
+
+  issue(st0, 0);
+  if (nst > 1) issue(st1, 1);
+  if (nst > 2) issue(st2, 2);
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  for (int t = 0; t < nst; t += 4) {
+    step(st0, st3, t, K0{});
+    step(st1, st0, t + 1, K1{});              // nst is even: stage t + 1 always exists
+    if (t + 2 < nst) {
+      step(st2, st1, t + 2, K0{});
+      step(st3, st2, t + 3, K1{});
+    }
+  }
+
+#pragma unroll
+  for (int b = 0; b < C::TM; ++b) {
+    const int64_t m = m0 + (wm * C::TM + b) * 32 + i;
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a)
+      store_tile<OUT>(p, acc[a][b], m, m < p.M, (int64_t)g * p.N + n0 + (wn * C::TN + a) * 32, q);
   }
 }
 
 // Tile configurations.  The choice depends only on (M, G, N, K), never on the
 // activation kind or the output mode, so every variant of one shape shares the
 // accumulation order.
-using CfgLarge = TileCfg<128, 128, 64, 64>;  // many tokens: 2 x 2 waves, 64 x 64 each
+using Cfg256 = BigCfg<256, 256, 2, 2>;   // E4M3 activations: 128 x 128 per wave
+using Cfg128 = BigCfg<128, 256, 1, 4>;   // E4M3 activations, N not a multiple of 256: 128 x 64 per wave
+// BF16 activations stage twice the bytes in registers and quantize them there:
+// half as many tokens per tile keeps the kernel within its registers (no spills).
+using CfgB256 = BigCfg<256, 128, 2, 2>;  // 128 x 64 per wave
+using CfgB128 = BigCfg<128, 128, 1, 4>;  // 128 x 32 per wave
 
 template <class C, bool X_BF16, int OUT>
 static hipError_t launch_cfg(const GemmArgs& p, int64_t G, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.N / C::BN), (unsigned)((p.M + C::BM - 1) / C::BM), (unsigned)G);
-  hipLaunchKernelGGL((gemm_kernel<C, X_BF16, OUT>), grid, dim3(kThreads), 0, stream, p);
+  const int n_tiles = (int)(p.N / C::BN);
+  const int m_tiles = (int)((p.M + C::BM - 1) / C::BM);
+  const int64_t total = G * n_tiles * (int64_t)m_tiles;
+  hipLaunchKernelGGL((big_gemm_kernel<C, X_BF16, OUT>), dim3((unsigned)total), dim3(C::THREADS), 0, stream, p, (int)G,
+                     m_tiles, n_tiles);
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, int OUT>
+static hipError_t launch_dl(const GemmArgs& p, int64_t G, hipStream_t stream) {
+  const int n_tiles = (int)(p.N / C::BN);
+  const int m_tiles = (int)((p.M + C::BM - 1) / C::BM);
+  const int64_t total = G * n_tiles * (int64_t)m_tiles;
+  hipLaunchKernelGGL((dl_gemm_kernel<C, OUT>), dim3((unsigned)total), dim3(256), 0, stream, p, (int)G, m_tiles,
+                     n_tiles);
+  return hipGetLastError();
+}
+
+// E4M3 activations: the direct-to-LDS kernel; BF16 activations: the register-
+// staged kernel, which quantizes on the way into LDS.  Both feed the MFMAs the
+// same bytes in the same K order (an output element's value does not depend on
+// the tile that holds it), so pre-quantized and BF16 activations give identical bits.
+template <class CQ, class CB>
 static hipError_t dispatch_kind_out(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t s) {
   if (x_bf16) {
-    if (out == OUT_BF16) return launch_cfg<C, true, OUT_BF16>(p, G, s);
-    if (out == OUT_MX) return launch_cfg<C, true, OUT_MX>(p, G, s);
-    return launch_cfg<C, true, OUT_BOTH>(p, G, s);
+    if (out == OUT_BF16) return launch_cfg<CB, true, OUT_BF16>(p, G, s);
+    if (out == OUT_MX) return launch_cfg<CB, true, OUT_MX>(p, G, s);
+    return launch_cfg<CB, true, OUT_BOTH>(p, G, s);
   }
-  if (out == OUT_BF16) return launch_cfg<C, false, OUT_BF16>(p, G, s);
-  if (out == OUT_MX) return launch_cfg<C, false, OUT_MX>(p, G, s);
-  return launch_cfg<C, false, OUT_BOTH>(p, G, s);
+  if (out == OUT_BF16) return launch_dl<CQ, OUT_BF16>(p, G, s);
+  if (out == OUT_MX) return launch_dl<CQ, OUT_MX>(p, G, s);
+  return launch_dl<CQ, OUT_BOTH>(p, G, s);
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream) {
-  return dispatch_kind_out<CfgLarge>(p, G, x_bf16, out, stream);
+  if (p.N % 256 == 0) return dispatch_kind_out<Cfg256, CfgB256>(p, G, x_bf16, out, stream);
+  return dispatch_kind_out<Cfg128, CfgB128>(p, G, x_bf16, out, stream);
 }
 
-// Kernel choice: a pure function of (M, G, N, K) -- never of the activation kind
-// or the output mode -- so those variants share one accumulation order.
+// Kernel choice between the few-token and the tiled family: a pure function of
+// (M, G, N, K) -- never of the activation kind or the output mode.
 constexpr int64_t kSkinnyMaxTokens = 256;
-constexpr int64_t kSliceSteps = 8;            // 128-K steps per K slice of the skinny kernel
+// The split-K kernel is sized for one resident round: two 256-thread workgroups per CU.
+constexpr int64_t kSkinnyTargetWorkgroups = 512;
 // The workspace always starts with this many bytes of arrival counters, whatever the
 // shape, so one shape's partial tiles never land on another shape's counters when
 // calls share a workspace.
@@ -199,21 +535,26 @@ constexpr int64_t kCounterBytes = 65536;
 GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K) {
   GemmPlan pl{};
   const int mt = M <= 32 ? 1 : 2;
-  const int chunks = (int)((M + 32 * mt - 1) / (32 * mt));
+  const int64_t chunks = (M + 63) / 64;
   const int64_t tiles = G * (N / 64) * chunks;
   pl.skinny = M <= kSkinnyMaxTokens && tiles * 4 <= kCounterBytes;
   if (!pl.skinny) {
-    pl.workgroups = G * (N / CfgLarge::BN) * ((M + CfgLarge::BM - 1) / CfgLarge::BM);
+    const int64_t bn = N % 256 == 0 ? 256 : 128;
+    pl.workgroups = G * (N / bn) * ((M + 255) / 256);     // E4M3 activations (BF16: twice as many)
     return pl;
   }
+  const int64_t ksteps = K / 128;
+  int64_t splits = kSkinnyTargetWorkgroups / (tiles > 0 ? tiles : 1);
+  const int64_t max_splits = ksteps / 4 > 1 ? ksteps / 4 : 1;     // at least two super-steps per split
+  splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
   pl.mt = mt;
-  pl.chunks = chunks;
+  pl.chunks = (int)chunks;
   pl.n_tiles = (int)(N / 64);
-  pl.splits = (int)((K / 128 + kSliceSteps - 1) / kSliceSteps);
-  pl.workgroups = tiles * pl.splits;
-  if (pl.splits > 1 && M > 0) {
+  pl.splits = (int)splits;
+  pl.workgroups = tiles * splits;
+  if (splits > 1 && M > 0) {
     pl.counter_bytes = kCounterBytes;
-    pl.workspace_bytes = pl.counter_bytes + tiles * pl.splits * (int64_t)(2 * pl.mt * 16 * 64) * 4;
+    pl.workspace_bytes = pl.counter_bytes + tiles * splits * (int64_t)(2 * mt * 16 * 64) * 4;
   }
   return pl;
 }

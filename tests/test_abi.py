@@ -132,14 +132,27 @@ def test_gemm_argument_errors():
     assert gemm(M=0, a=None, d=None) == B.MXFP8_OK
 
 
+def test_size_limits_of_tile_addressing():
+    """256-row tiles are addressed with 32-bit offsets: row strides above 2^23 bytes and K above 2^22 are
+    rejected before any launch (the documented limits)."""
+    assert gemm(ld_a=(1 << 23) + 16) == B.MXFP8_ERR_SHAPE                   # E4M3 rows, bytes
+    assert gemm(kind=B.MXFP8_ACT_BF16, ld_a=(1 << 22) + 8) == B.MXFP8_ERR_SHAPE   # BF16 rows: 2 bytes each
+    assert gemm(ld_asf=(1 << 16)) == B.MXFP8_ERR_SHAPE                      # scale rows: 4 bytes per word
+    assert gemm(K=(1 << 22) + 128) == B.MXFP8_ERR_SHAPE
+    assert einsum(K=(1 << 22) + 128) == B.MXFP8_ERR_SHAPE
+    assert LIB.fp8_gemm_nt_workspace_size(4, 256, (1 << 22) + 128) == -1
+    assert LIB.grouped_fp8_einsum_workspace_size(4, 2, (1 << 22) + 128, 128) == -1
+
+
 @pytest.mark.skipif(HAVE_GPU, reason="a GPU is present")
 def test_valid_gemm_reports_missing_device():
     assert gemm() == B.MXFP8_ERR_DEVICE
 
 
 def test_workspace_sizes():
-    # one 1024-deep K slice needs no split-K scratch; deeper K does (decode range only)
-    assert LIB.grouped_fp8_einsum_workspace_size(64, 8, 1024, 1024) == 0
+    # a K range shorter than two 256-deep super-steps per split is never split (no scratch); deeper K is
+    # split across workgroups in the decode range only
+    assert LIB.grouped_fp8_einsum_workspace_size(64, 8, 512, 1024) == 0
     need = LIB.grouped_fp8_einsum_workspace_size(64, 8, 4096, 1024)
     assert need > 0 and need % 256 == 0
     assert LIB.fp8_gemm_nt_workspace_size(64, 5120, 8192) > 0

@@ -57,7 +57,8 @@ def exact_operands(rng, rows, cols):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (7, 256, 512), (33, 384, 1024), (130, 256, 4096),
-                                   (257, 128, 256), (5, 128, 1152), (40, 256, 2176), (64, 512, 8192)])
+                                   (257, 128, 256), (5, 128, 1152), (40, 256, 2176), (64, 512, 8192),
+                                   (300, 512, 1024), (513, 384, 512), (1024, 256, 4096), (777, 768, 128)])
 def test_gemm_exact_regime_bitexact(lib, M, N, K):
     rng = np.random.default_rng(1000 + M)
     aq, asf = exact_operands(rng, M, K)
@@ -68,7 +69,8 @@ def test_gemm_exact_regime_bitexact(lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,G,K,N", [(4, 2, 256, 128), (45, 3, 512, 256), (96, 8, 128, 128), (3, 2, 1152, 128),
-                                     (64, 2, 4096, 256)])
+                                     (64, 2, 4096, 256), (600, 2, 512, 512), (257, 3, 256, 128),
+                                     (520, 2, 1024, 384)])
 def test_einsum_exact_regime_bitexact(lib, M, G, K, N):
     rng = np.random.default_rng(2000 + M)
     xq, xsf = exact_operands(rng, M, G * K)
@@ -81,6 +83,51 @@ def test_einsum_exact_regime_bitexact(lib, M, G, K, N):
     assert np.array_equal(to_np(z_b), zb)
     assert np.array_equal(to_np(z_q), oq)
     assert np.array_equal(to_np(z_sf), osf)
+
+
+EXACT_VALUES = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], dtype=np.float32)
+
+
+def _nan_padded(rows_valid, t, fill):
+    """A device tensor whose storage continues past row `rows_valid` with `fill` (a NaN pattern), viewed
+    as its first rows_valid rows: a kernel that reads a row past M meets the NaN."""
+    big = torch.empty((rows_valid + 64,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev())
+    big.view(torch.uint8 if t.dtype == torch.uint8 else (torch.int16 if t.dtype == torch.bfloat16 else torch.int32))\
+        .fill_(fill)
+    big[:rows_valid] = t
+    return big[:rows_valid]
+
+
+@pytest.mark.parametrize("M", [7, 33, 290, 300])
+def test_rows_past_m_are_never_read(lib, M):
+    """Exact regime (BF16 values that quantize exactly; sums exact in fp32) with activation storage that
+    continues past row M with NaN bytes: every output must still equal the oracle bit for bit, for BF16
+    activations (quantized in the load path) and for E4M3 activations, in the GEMM and the einsum."""
+    rng = np.random.default_rng(300 + M)
+    N, K = 512, 1024
+    a = rng.choice(EXACT_VALUES, size=(M, K))
+    bq, bsf = exact_operands(rng, N, K)
+    ref = mx.bf16_round(a.astype(np.float64) @ (mx.E4M3_TABLE[bq] * np.repeat(
+        np.ldexp(1.0, mx.unpack_scales(bsf).astype(np.int64) - 127), 32, axis=1)).T)
+    at = _nan_padded(M, torch.from_numpy(a).to(torch.bfloat16).to(dev()), 0x7FC0)
+    b_t, bsf_t = u8_to_dev(bq), i32_to_dev(bsf)
+    assert np.array_equal(to_np(lib.fp8_gemm_nt(at, None, b_t, bsf_t)), ref)
+    aq, asf = lib.mxfp8_quantize(at)
+    aq_p, asf_p = _nan_padded(M, aq, 0x7F), _nan_padded(M, asf, -1)
+    assert np.array_equal(to_np(lib.fp8_gemm_nt(aq_p, asf_p, b_t, bsf_t)), ref)
+    # einsum, two groups, BF16 and E4M3 x
+    G, Ng = 2, 256
+    x = rng.choice(EXACT_VALUES, size=(M, G * K))
+    wq, wsf = exact_operands(rng, G * Ng, K)
+    w_t, wsf_t = u8_to_dev(wq.reshape(G, Ng, K)), i32_to_dev(wsf.reshape(G, Ng, K // 128))
+    xq_o, xsf_o = mx.quantize(mx.bf16_round(x))
+    z_ref = mx.bf16_round(cr.grouped_einsum(xq_o, xsf_o, wq.reshape(G, Ng, K), wsf.reshape(G, Ng, K // 128),
+                                            G, K, Ng))
+    xt = _nan_padded(M, torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(dev()), 0x7FC0)
+    assert np.array_equal(to_np(lib.grouped_fp8_einsum(xt, None, w_t, wsf_t, out="bf16")), z_ref)
+    xq, xsf = lib.mxfp8_quantize(xt)
+    zq = lib.grouped_fp8_einsum(_nan_padded(M, xq, 0x7F), _nan_padded(M, xsf, -1), w_t, wsf_t, out="bf16")
+    assert np.array_equal(to_np(zq), z_ref)
 
 
 def test_split_k_workspace_counters_return_to_zero(lib):
@@ -194,7 +241,7 @@ def test_fused_z_equals_quantized_own_bf16(lib, name):
     assert torch.equal(z_q2, z_q) and torch.equal(z_sf2, z_sf) and torch.equal(z_b2, z_b)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "ragged"])
 def test_prequantized_x_equals_in_kernel_quantization(lib, name):
     c = get_case(name, lib)
     xq, xsf = lib.mxfp8_quantize(c.x)
