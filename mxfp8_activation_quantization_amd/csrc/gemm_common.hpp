@@ -82,6 +82,48 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f& acc, i
   }
 }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kRawBufferFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked
+
+// Direct-to-LDS loads are written as inline assembly on purpose: the compiler
+// tracks its own LDS-DMA builtins conservatively and would wait for every one in
+// flight before each LDS read, which would undo the pipeline.  The kernel does
+// its own counting (s_waitcnt vmcnt) and its own barriers.  The buffer resource
+// is built by hand: base address, stride 0, byte range, raw-buffer flags.
+struct Rsrc {
+  v4i v;
+};
+
+__device__ __forceinline__ Rsrc make_rsrc_sgpr(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  Rsrc r;
+  r.v = v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)kRawBufferFlags};
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// 64 lanes x 16 bytes from rsrc + voff + soff into LDS [lds, lds + 1024), lane l at lds + 16 l.
+__device__ __forceinline__ void dl_load16(const Rsrc& r, const void* lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
+}
+
+// 64 lanes x 4 bytes, lane l at lds + 4 l.
+__device__ __forceinline__ void dl_load4(const Rsrc& r, const void* lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier for LDS exchange inside software pipelines: waits for this
 // wave's LDS operations only, then s_barrier.  __syncthreads() would also wait
 // for every global load still in flight (its release fence covers all memory),

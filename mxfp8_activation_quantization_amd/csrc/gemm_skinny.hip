@@ -29,7 +29,6 @@
 
 namespace mx {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -161,6 +160,72 @@ __device__ __forceinline__ void store_super(const Super<X_BF16>& st, uint8_t* sW
 
 }  // namespace
 
+// The end of a work item: with one split the tile goes straight to the epilogue.
+// Otherwise the item publishes its partial tile and the last of the S items of
+// the tile to arrive adds the partials in split order 0, 1, ..., S-1 and runs the
+// epilogue.  The items of a tile may run on different XCDs, whose L2 caches are
+// not coherent with each other, so partials move with 16-byte buffer accesses
+// that bypass L1 and L2 (sc0 sc1) and the counter with a relaxed system-scope
+// atomic: a writer waits until its stores are complete before it bumps the
+// counter, and the last one reads the partials from memory.  Partial layout per
+// split: [rt][tt][lane][16 floats].  All threads of the workgroup must call this.
+template <int MT, int OUT>
+__device__ __forceinline__ void finish_tile(const GemmArgs& p, const v16f& acc, int tc, int s, int S, int rt, int tt,
+                                            int lane, int tid, int64_t nb, int64_t m, bool computes, int* s_last) {
+  const int q = lane >> 5;
+  if (S == 1) {
+    if (computes) store_tile<OUT>(p, acc, m, m < p.M, nb, q);
+    return;
+  }
+  constexpr int TILE_FLOATS = 2 * MT * 16 * 64;
+  constexpr int TILE_BYTES = TILE_FLOATS * 4;
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_partials + (int64_t)tc * S * TILE_FLOATS, 0, S * TILE_BYTES, kRsrcFlags);
+  const int my_off = ((rt * MT + tt) * 64 + lane) * 64;     // bytes within a split's tile
+  if (computes) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const v4i v = {__float_as_int(acc[4 * k]), __float_as_int(acc[4 * k + 1]), __float_as_int(acc[4 * k + 2]),
+                     __float_as_int(acc[4 * k + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rp, s * TILE_BYTES + my_off + 16 * k, 0, kUncached);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    *s_last = __hip_atomic_fetch_add(&p.ws_counters[tc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+              (uint32_t)(S - 1);
+  __syncthreads();
+  if (!*s_last || !computes) return;
+
+  // the last item: each wave sums its own 32 x 32 tile over the splits, in split order
+  v16f tot = zero16();
+  for (int s0 = 0; s0 < S; s0 += 2) {
+    v4i ld[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        ld[u][k] = s0 + u < S ? __builtin_amdgcn_raw_buffer_load_b128(rp, (s0 + u) * TILE_BYTES + my_off + 16 * k, 0,
+                                                                      kUncached)
+                              : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (s0 + u < S) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          tot[4 * k] += __int_as_float(ld[u][k].x);
+          tot[4 * k + 1] += __int_as_float(ld[u][k].y);
+          tot[4 * k + 2] += __int_as_float(ld[u][k].z);
+          tot[4 * k + 3] += __int_as_float(ld[u][k].w);
+        }
+      }
+    }
+  }
+  store_tile<OUT>(p, tot, m, m < p.M, nb, q);
+  if (tid == 0) __hip_atomic_store(&p.ws_counters[tc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 template <int MT, bool X_BF16, int OUT>
 __global__ __launch_bounds__(kThreads) void splitk_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   __shared__ __attribute__((aligned(1024))) uint8_t sW[2][kSuper * kStepBytes];
@@ -235,66 +300,177 @@ __global__ __launch_bounds__(kThreads) void splitk_kernel(GemmArgs p, int G, int
     if (ss + 1 < nss) body(st1, ss + 1, 1);
   }
 
-  const int64_t nb = n_row0 + rt * 32;
-  const int64_t m = m_first + tt * 32 + i;
-  if (S == 1) {
-    if (computes) store_tile<OUT>(p, acc, m, m < p.M, nb, q);
-    return;
+  finish_tile<MT, OUT>(p, acc, tc, s, S, rt, tt, lane, tid, n_row0 + rt * 32, m_first + tt * 32 + i, computes,
+                       &s_last);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 activations: the weight-streaming kernel proper.
+//
+// Both operands are codes, so every byte goes from memory straight into LDS
+// (buffer_load ... lds) and the pipeline depth is bounded by LDS, not registers:
+// a ring of kRing stages of kStageSteps 128-deep steps (64 weight rows and 64 token
+// rows x 128 bytes per step: 32 KB per stage), with the loads of stage t + kRing - 1
+// issued while stage t is multiplied.  One workgroup per CU keeps 48 KB of weights
+// in flight per CU, enough to cover HBM latency at full bandwidth; two steps per
+// stage halve the barriers and the LDS-read -> MFMA latency each stage exposes.  The scale words of the whole K range (up
+// to kMaxSteps steps) are fetched once, at the start, into two tables: per step
+// they would be 64 scattered 4-byte reads per operand.
+//
+// Stage layout of an operand (64 rows x 8 chunks of 16 bytes): chunk c of row r
+// sits in slot 8r + (c ^ g8(r)), g8(r) = ((r >> 1) & 7) ^ ((r & 1) << 2).  One
+// load instruction fills 1 KB of consecutive slots = 8 whole rows (row-contiguous
+// 128-byte reads), and the 16 (or 8) lanes of a fragment read -- 16 rows, one
+// chunk -- hit distinct 16-byte bank groups.  Scale tables: row r holds the words
+// of steps k_lo .. k_lo + 31 as eight 16-byte chunks, chunk c at position c ^ (r & 7).
+// A lane's fragment (row i, chunks 4KS + q and 4KS + 2 + q) is the same bytes in
+// the same MFMA order as in the register-staged kernel above, which uses the same
+// split plan, so E4M3 and BF16 activations give identical bits.
+constexpr int kRing = 4;
+constexpr int kStageSteps = 2;
+constexpr int kMaxSteps = 32;
+
+__device__ __forceinline__ int g8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+__device__ __forceinline__ v8i ring_frag(const uint8_t* op, int T, int KS, int lane) {
+  const int i = lane & 31, q = lane >> 5, r = 32 * T + i, g = g8(r);
+  const uint8_t* b = op + 128 * r;
+  return frag(*reinterpret_cast<const uint4*>(b + 16 * ((4 * KS + q) ^ g)),
+              *reinterpret_cast<const uint4*>(b + 16 * ((4 * KS + 2 + q) ^ g)));
+}
+
+__device__ __forceinline__ uint32_t table_word(const uint32_t* tab, int r, int j) {
+  return tab[r * 32 + (((j >> 2) ^ (r & 7)) << 2) + (j & 3)];
+}
+
+struct RingStage {
+  uint8_t w[kStageSteps][64 * 128];
+  uint8_t x[kStageSteps][64 * 128];
+};
+
+// Waits until at most n stages of this wave's loads (L instructions each) are in flight.
+template <int L>
+__device__ __forceinline__ void wait_stages(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<L>(); break;
+    default: wait_vmcnt<2 * L>(); break;
+  }
+}
+
+template <int MT, int OUT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
+  static_assert(kRing == 4, "wait_stages covers up to kRing - 2 stages in flight");
+  constexpr int L = 4 * kStageSteps;     // load instructions per wave and stage: per step 2 weight, 2 activation
+  __shared__ __attribute__((aligned(1024))) RingStage ring[kRing];
+  __shared__ __attribute__((aligned(1024))) uint32_t wtab[64 * kMaxSteps];
+  __shared__ __attribute__((aligned(1024))) uint32_t xtab[64 * kMaxSteps];
+  __shared__ int s_last;
+
+  const int total = G * n_tiles * chunks * S;
+  const int wi = xcd_work_index((int)blockIdx.x, total);
+  const int s = wi % S;
+  const int rest = wi / S;
+  const int chunk = rest % chunks;
+  const int tile = rest / chunks;
+  const int g = tile / n_tiles, nt = tile % n_tiles;
+  const int tc = tile * chunks + chunk;
+
+  const int tid = threadIdx.x, lane = tid & 63, i = lane & 31, q = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = wave & 1, tt = wave >> 1;
+  const bool computes = tt < MT;
+
+  const int ksteps = (int)(p.K / 128);
+  const int k_lo = (int)((int64_t)s * ksteps / S);
+  const int k_hi = (int)((int64_t)(s + 1) * ksteps / S);
+  const int nsteps = k_hi - k_lo;                 // <= kMaxSteps (the plan guarantees it)
+  const int nst = (nsteps + kStageSteps - 1) / kStageSteps;
+  const int64_t n_row0 = (int64_t)g * p.N + (int64_t)nt * kTileRows;
+  const int64_t m_first = (int64_t)chunk * kChunkTokens;
+  const int64_t m_rows = p.M - m_first < kChunkTokens ? p.M - m_first : kChunkTokens;
+  const int ldw = (int)p.K, ldx = (int)p.ld_x, ldxs = (int)(p.ld_xsf * 4);
+  const int xcol0 = (int)((int64_t)g * p.K), xsfcol0 = g * ksteps * 4;
+  const Rsrc rw = make_rsrc_sgpr(p.w + n_row0 * p.K, (int64_t)kTileRows * p.K);
+  const Rsrc rws = make_rsrc_sgpr(p.w_sf + n_row0 * ksteps, (int64_t)kTileRows * ksteps * 4);
+  // Activation ranges end at row m_rows and the row part of every activation
+  // offset is in the per-lane register (the part the range check covers), so rows
+  // past M arrive as zeros and nothing past row M is read.  The scale tables may
+  // read up to 31 words past a row's K range: the next row's words (unused), or
+  // zeros past the end of the buffer.
+  const Rsrc rx = make_rsrc_sgpr(static_cast<const uint8_t*>(p.x) + m_first * ldx, m_rows * ldx);
+  const Rsrc rxs = make_rsrc_sgpr(p.x_sf + m_first * p.ld_xsf, m_rows * ldxs);
+
+  // per-lane offsets: instruction j of this wave covers rows 8n .. 8n+7, n = 4j + wave
+  int vw[2], vx[2], vts[2], vtx[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = 4 * j + wave, r = 8 * n + (lane >> 3), c = (lane & 7) ^ g8(r), ct = (lane & 7) ^ (r & 7);
+    vw[j] = r * ldw + c * 16;
+    vx[j] = r * ldx + c * 16;
+    // scale table chunk ct = steps 4ct .. 4ct+3 of the range; the whole offset is in the
+    // per-lane register so that the range check sees it (no read past a buffer's end)
+    vts[j] = (r * ksteps + k_lo) * 4 + ct * 16;
+    vtx[j] = r * ldxs + xsfcol0 + k_lo * 4 + ct * 16;
   }
 
-  // Split K: publish this item's partial tile.  The items of a tile may run on
-  // different XCDs, whose L2 caches are not coherent with each other, so partials
-  // move with 16-byte buffer accesses that bypass L1 and L2 (sc0 sc1), and the
-  // counter with a relaxed system-scope atomic: a writer waits until its stores
-  // are complete before it bumps the counter, and the last one reads the partials
-  // from memory.  Partial layout per split: [rt][tt][lane][16 floats].
-  constexpr int TILE_FLOATS = 2 * MT * 16 * 64;
-  constexpr int TILE_BYTES = TILE_FLOATS * 4;
-  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-      p.ws_partials + (int64_t)tc * S * TILE_FLOATS, 0, S * TILE_BYTES, kRsrcFlags);
-  const int my_off = ((rt * MT + tt) * 64 + lane) * 64;     // bytes within a split's tile
-  if (computes) {
+  // scale tables first (they complete before any stage: loads finish in issue order)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const v4i v = {__float_as_int(acc[4 * k]), __float_as_int(acc[4 * k + 1]), __float_as_int(acc[4 * k + 2]),
-                     __float_as_int(acc[4 * k + 3])};
-      __builtin_amdgcn_raw_buffer_store_b128(v, rp, s * TILE_BYTES + my_off + 16 * k, 0, kUncached);
+  for (int j = 0; j < 2; ++j) {
+    const int n = 4 * j + wave;
+    dl_load16(rws, wtab + n * 256, vts[j], 0);
+    dl_load16(rxs, xtab + n * 256, vtx[j], 0);
+  }
+
+  // A stage's second step past the range (odd step count) loads the last step
+  // again -- valid addresses -- and is not multiplied.
+  auto issue = [&](int t) {
+    RingStage& st = ring[t % kRing];
+#pragma unroll
+    for (int h = 0; h < kStageSteps; ++h) {
+      const int kk = k_lo + kStageSteps * t + h, k = kk < k_hi ? kk : k_hi - 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = 4 * j + wave;
+        dl_load16(rw, st.w[h] + n * 1024, vw[j], k * 128);
+        dl_load16(rx, st.x[h] + n * 1024, vx[j], xcol0 + k * 128);
+      }
     }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&p.ws_counters[tc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
-             (uint32_t)(S - 1);
-  __syncthreads();
-  if (!s_last || !computes) return;
+  };
 
-  // the last item: each wave sums its own 32 x 32 tile over the splits, in split order
-  v16f tot = zero16();
-  for (int s0 = 0; s0 < S; s0 += 2) {
-    v4i ld[2][4];
+  v16f acc = zero16();
+  const int pre = nst < kRing - 1 ? nst : kRing - 1;
+  for (int t = 0; t < pre; ++t) issue(t);
+  for (int t = 0; t < nst; ++t) {
+    // stage t's loads are done when at most the later issued stages remain in flight
+    const int later = (nst - 1 - t) < (kRing - 2) ? (nst - 1 - t) : (kRing - 2);
+    wait_stages<L>(later);
+    asm volatile("s_barrier" ::: "memory");       // every wave's loads of stage t landed; stage t-1 is free
+    if (t + kRing - 1 < nst) issue(t + kRing - 1);
+    if (computes) {
+      const RingStage& st = ring[t % kRing];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        ld[u][k] = s0 + u < S ? __builtin_amdgcn_raw_buffer_load_b128(rp, (s0 + u) * TILE_BYTES + my_off + 16 * k, 0,
-                                                                      kUncached)
-                              : v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (s0 + u < S) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          tot[4 * k] += __int_as_float(ld[u][k].x);
-          tot[4 * k + 1] += __int_as_float(ld[u][k].y);
-          tot[4 * k + 2] += __int_as_float(ld[u][k].z);
-          tot[4 * k + 3] += __int_as_float(ld[u][k].w);
+      for (int h = 0; h < kStageSteps; ++h) {
+        const int j = kStageSteps * t + h;
+        if (j < nsteps) {
+          const int sw = (int)(table_word(wtab, rt * 32 + i, j) >> (8 * q));
+          const int sx = (int)(table_word(xtab, tt * 32 + i, j) >> (8 * q));
+          acc = mfma_scaled<0>(ring_frag(st.w[h], rt, 0, lane), ring_frag(st.x[h], tt, 0, lane), acc, sw, sx);
+          acc = mfma_scaled<2>(ring_frag(st.w[h], rt, 1, lane), ring_frag(st.x[h], tt, 1, lane), acc, sw, sx);
         }
       }
     }
   }
-  store_tile<OUT>(p, tot, m, m < p.M, nb, q);
-  if (tid == 0) __hip_atomic_store(&p.ws_counters[tc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  finish_tile<MT, OUT>(p, acc, tc, s, S, rt, tt, lane, tid, n_row0 + rt * 32, m_first + tt * 32 + i, computes,
+                       &s_last);
+}
+
+template <int MT, int OUT>
+static hipError_t launch_stream(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
+  hipLaunchKernelGGL((stream_kernel<MT, OUT>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p, (int)G,
+                     plan.n_tiles, plan.chunks, plan.splits);
+  return hipGetLastError();
 }
 
 template <int MT, bool X_BF16, int OUT>
@@ -312,9 +488,9 @@ static hipError_t dispatch(const GemmArgs& p, const GemmPlan& plan, int64_t G, b
     if (out == OUT_MX) return launch_mt<MT, true, OUT_MX>(p, plan, G, s);
     return launch_mt<MT, true, OUT_BOTH>(p, plan, G, s);
   }
-  if (out == OUT_BF16) return launch_mt<MT, false, OUT_BF16>(p, plan, G, s);
-  if (out == OUT_MX) return launch_mt<MT, false, OUT_MX>(p, plan, G, s);
-  return launch_mt<MT, false, OUT_BOTH>(p, plan, G, s);
+  if (out == OUT_BF16) return launch_stream<MT, OUT_BF16>(p, plan, G, s);
+  if (out == OUT_MX) return launch_stream<MT, OUT_MX>(p, plan, G, s);
+  return launch_stream<MT, OUT_BOTH>(p, plan, G, s);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,

@@ -38,7 +38,6 @@
 
 namespace mx {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked
 
@@ -301,38 +300,6 @@ __device__ __forceinline__ v8i dl_read_frag(const uint8_t* stage_op, int T, int 
   return frag(*reinterpret_cast<const uint4*>(b + 16 * (q ^ gi)), *reinterpret_cast<const uint4*>(b + 16 * ((2 + q) ^ gi)));
 }
 
-// Direct-to-LDS loads are written as inline assembly on purpose: the compiler
-// tracks its own LDS-DMA builtins conservatively and would wait for every one in
-// flight before each LDS read, which would undo the pipeline.  The kernel does
-// its own counting (s_waitcnt vmcnt) and its own barriers.  The buffer resource
-// is built by hand: base address, stride 0, byte range, raw-buffer flags.
-struct Rsrc {
-  v4i v;
-};
-
-__device__ __forceinline__ Rsrc make_rsrc_sgpr(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  Rsrc r;
-  r.v = v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)kRsrcFlags};
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-// 64 lanes x 16 bytes from rsrc + voff + soff into LDS [lds, lds + 1024), lane l at lds + 16 l.
-__device__ __forceinline__ void dl_load16(const Rsrc& r, const void* lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
-}
-
-// 64 lanes x 4 bytes, lane l at lds + 4 l.
-__device__ __forceinline__ void dl_load4(const Rsrc& r, const void* lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
-}
-
 template <class C>
 struct DlStage {
   uint8_t w[C::BN * 64];
@@ -525,8 +492,9 @@ hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, bool x_bf16, int out,
 // Kernel choice between the few-token and the tiled family: a pure function of
 // (M, G, N, K) -- never of the activation kind or the output mode.
 constexpr int64_t kSkinnyMaxTokens = 256;
-// The split-K kernel is sized for one resident round: two 256-thread workgroups per CU.
-constexpr int64_t kSkinnyTargetWorkgroups = 512;
+// The few-token kernels are sized for one resident round: one workgroup per CU.
+constexpr int64_t kSkinnyTargetWorkgroups = 256;
+constexpr int64_t kSkinnyMaxSteps = 32;       // 128-deep steps per split (the streaming kernel's scale tables)
 // The workspace always starts with this many bytes of arrival counters, whatever the
 // shape, so one shape's partial tiles never land on another shape's counters when
 // calls share a workspace.
@@ -546,7 +514,9 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K) {
   const int64_t ksteps = K / 128;
   int64_t splits = kSkinnyTargetWorkgroups / (tiles > 0 ? tiles : 1);
   const int64_t max_splits = ksteps / 4 > 1 ? ksteps / 4 : 1;     // at least two super-steps per split
+  const int64_t min_splits = (ksteps + kSkinnyMaxSteps - 1) / kSkinnyMaxSteps;   // scale tables hold 32 steps
   splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
+  splits = splits < min_splits ? min_splits : splits;
   pl.mt = mt;
   pl.chunks = (int)chunks;
   pl.n_tiles = (int)(N / 64);
