@@ -3,19 +3,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|tiny|prefill|long]
 
 One step = one pass of the chain over one batch of synthetic tokens:
-grouped_fp8_einsum (wo_a, BF16 x quantized in the load path, MXFP8 epilogue)
-then fp8_gemm_nt (wo_b, BF16 out), replayed from a HIP graph.  Inputs are
-resident in HBM before the timed region.  Every step uses the next of R
-rotating copies of the inputs, weights and outputs (together >= 600 MB, more
+mxfp8_quantize (BF16 x -> MXFP8), grouped_fp8_einsum (wo_a, MXFP8 epilogue
+writing z), fp8_gemm_nt (wo_b on (z, sf), BF16 out), replayed from a HIP graph.
+Inputs are resident in HBM before the timed region.  Every step uses the next of
+R rotating copies of the inputs, weights and outputs (together >= 600 MB, more
 than the 256 MB Infinity Cache), so each step reads its weights cold, as the
 layers of a model do.
 
 Printed: one JSON line.  `value` is chain TFLOP/s at the configuration's token
-count; `ms_per_step` its time per call.  Besides the headline arm it reports the
-three-launch arm (standalone mxfp8_quantize first) and the unfused arm (BF16 z
-re-quantized by a separate launch), per-kernel durations from HIP events on the
-launch stream, the dominant kernel's roofline fraction, and the CPU oracle timed
-on this host's cores.
+count; `ms_per_step` its time per call.  Besides the headline arm ("chain") it
+reports the arm whose einsum quantizes BF16 x in its load path ("x_fused", two
+launches) and the unfused arm ("unfused": BF16 z re-quantized by a separate
+launch, the arrangement the fused epilogue replaces), per-kernel durations from
+HIP events on the launch stream, the dominant kernel's roofline fraction, and the
+CPU oracle timed on this host's cores.
 """
 from __future__ import annotations
 
@@ -36,6 +37,7 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 ROTATE_BYTES = 600 << 20
 KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_skinny.hip", "gemm_common.hpp", "quantize.hip", "mx_device.hpp"]
+KERNEL_NAMES = {"quantize": "mxfp8_quantize", "einsum": "grouped_fp8_einsum", "gemm": "fp8_gemm_nt"}
 
 
 def kernel_source_hash() -> str:
@@ -47,19 +49,20 @@ def kernel_source_hash() -> str:
 
 
 def chain_bytes(M, G, K, N, P):
-    """Algorithmic HBM bytes of each launch (weights once, activations once)."""
+    """Algorithmic HBM bytes of each launch of the chain (every operand read once, every result written once)."""
     wa = G * N * K + G * N * (K // 128) * 4
     wb = P * G * N + P * (G * N // 128) * 4
+    x_mx = M * (G * K + (G * K // 128) * 4)
     z_mx = M * (G * N + (G * N // 128) * 4)
     return {
-        "einsum": M * G * K * 2 + wa + z_mx,              # BF16 x in, MXFP8 z out
+        "quantize": M * G * K * 2 + x_mx,                  # BF16 x in, MXFP8 x out
+        "einsum": x_mx + wa + z_mx,                        # MXFP8 x in, MXFP8 z out
         "gemm": z_mx + wb + M * P * 2,                     # MXFP8 z in, BF16 out
-        "quantize_x": M * G * K * 2 + M * (G * K + (G * K // 128) * 4),
     }
 
 
 def chain_flops(M, G, K, N, P):
-    return {"einsum": 2 * M * G * K * N, "gemm": 2 * M * G * N * P}
+    return {"quantize": 0, "einsum": 2 * M * G * K * N, "gemm": 2 * M * G * N * P}
 
 
 def threads_used() -> int:
@@ -133,7 +136,7 @@ def time_arm_graphs(torch, graphs, stream, steps, warmup):
 
 
 def sweep(torch, L, Ms, dims, w, stream, args):
-    """Fused and prequant chain µs/call over token counts, weights rotated as in the headline run."""
+    """Chain and x_fused µs/call over token counts, weights rotated as in the headline run."""
     G, K, N, P = dims
     out = []
     gen = torch.Generator(device="cuda")
@@ -146,7 +149,7 @@ def sweep(torch, L, Ms, dims, w, stream, args):
                  "wa_q": w["wa_q"].clone(), "wa_sf": w["wa_sf"].clone(),
                  "wb_q": w["wb_q"].clone(), "wb_sf": w["wb_sf"].clone()} for r in range(R)]
         res = {"M": M}
-        for arm in ("fused", "prequant"):
+        for arm in ("chain", "x_fused"):
             graphs = []
             for s in sets:
                 g = torch.cuda.CUDAGraph()
@@ -162,13 +165,12 @@ def sweep(torch, L, Ms, dims, w, stream, args):
             del graphs
         flop = sum(chain_flops(M, G, K, N, P).values())
         nb = chain_bytes(M, G, K, N, P)
-        us = min(res["fused_us"], res["prequant_us"])
-        res["tflops_fused"] = flop / (res["fused_us"] * 1e-6) / 1e12
-        res["hbm_frac_fused"] = (nb["einsum"] + nb["gemm"]) / (res["fused_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
-        res["mfma_frac_fused"] = res["tflops_fused"] / FP8_PEAK_TFLOPS
-        res["best_us"] = us
-        print(f"[bench] sweep M={M}: fused {res['fused_us']:.2f} us, prequant {res['prequant_us']:.2f} us, "
-              f"{res['tflops_fused']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        us = res["chain_us"]
+        res["tflops"] = flop / (us * 1e-6) / 1e12
+        res["hbm_frac"] = sum(nb.values()) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+        res["mfma_frac"] = res["tflops"] / FP8_PEAK_TFLOPS
+        print(f"[bench] sweep M={M}: chain {us:.2f} us, x_fused {res['x_fused_us']:.2f} us, "
+              f"{res['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         out.append(res)
         del sets, x
         torch.cuda.empty_cache()
@@ -182,9 +184,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--arms", default="fused,prequant,unfused")
+    ap.add_argument("--arms", default="chain,x_fused,unfused")
     ap.add_argument("--sweep", default="",
-                    help="comma-separated token counts: also time the fused and prequant chains at each "
+                    help="comma-separated token counts: also time the chain and x_fused arms at each "
                          "(decode-config weights, x drawn on the device) and report them under 'sweep'")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB 5 times (HBM counter calibration)")
@@ -227,6 +229,8 @@ def main():
             "x": x0 if r == 0 else x0.clone(),
             "wa_q": wa_q0 if r == 0 else wa_q0.clone(), "wa_sf": wa_sf0 if r == 0 else wa_sf0.clone(),
             "wb_q": wb_q0 if r == 0 else wb_q0.clone(), "wb_sf": wb_sf0 if r == 0 else wb_sf0.clone(),
+            "x_q": torch.empty((M, G * K), dtype=torch.uint8, device=dev),
+            "x_sf": torch.empty((M, G * K // 128), dtype=torch.int32, device=dev),
             "z_q": torch.empty((M, G * N), dtype=torch.uint8, device=dev),
             "z_sf": torch.empty((M, G * N // 128), dtype=torch.int32, device=dev),
             "out": torch.empty((M, P), dtype=torch.bfloat16, device=dev),
@@ -236,20 +240,24 @@ def main():
 
     stream = torch.cuda.Stream()
 
-    def launch_fused(s, ev=None):
+    def launch_chain(s, ev=None):
+        """The headline chain into preallocated buffers; optional events around each launch."""
         if ev is not None:
             ev[0].record(stream)
-        L.grouped_fp8_einsum(s["x"], None, s["wa_q"], s["wa_sf"], out="mxfp8", z_q=s["z_q"], z_sf=s["z_sf"],
-                             stream=stream)
+        L.mxfp8_quantize(s["x"], q=s["x_q"], sf=s["x_sf"], stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        L.fp8_gemm_nt(s["z_q"], s["z_sf"], s["wb_q"], s["wb_sf"], d=s["out"], stream=stream)
+        L.grouped_fp8_einsum(s["x_q"], s["x_sf"], s["wa_q"], s["wa_sf"], out="mxfp8", z_q=s["z_q"], z_sf=s["z_sf"],
+                             stream=stream)
         if ev is not None:
             ev[2].record(stream)
+        L.fp8_gemm_nt(s["z_q"], s["z_sf"], s["wb_q"], s["wb_sf"], d=s["out"], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
 
     def launch_arm(arm, s):
-        if arm == "fused":
-            launch_fused(s)
+        if arm == "chain":
+            launch_chain(s)
         else:
             L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm, stream=stream)
 
@@ -291,29 +299,29 @@ def main():
         print(f"[bench] arm {arm}: {ms_ev * 1e3:.2f} us/call (graph replay)", file=sys.stderr, flush=True)
         del graphs
 
-    # per-kernel durations: HIP events on the launch stream around each kernel of the headline arm
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # per-kernel durations: HIP events on the launch stream around each kernel of the headline chain
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            launch_fused(sets[i % R])
+            launch_chain(sets[i % R])
         torch.cuda.synchronize()
         for i in range(args.steps):
-            launch_fused(sets[i % R], evs[i])
+            launch_chain(sets[i % R], evs[i])
     torch.cuda.synchronize()
-    t_einsum = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
-    t_gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    t_k = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
+           for j, k in enumerate(("quantize", "einsum", "gemm"))}
 
     flops = chain_flops(M, G, K, N, P)
     nbytes = chain_bytes(M, G, K, N, P)
-    total_flop = flops["einsum"] + flops["gemm"]
-    head = results.get("fused", next(iter(results.values())))
+    total_flop = sum(flops.values())
+    head = results.get("chain", next(iter(results.values())))
     us = head["us_per_call"]
     value = total_flop / (us * 1e-6) / 1e12
 
-    dom = "einsum" if t_einsum >= t_gemm else "gemm"
-    t_dom = t_einsum if dom == "einsum" else t_gemm
-    hbm_bound = (total_flop / (nbytes["einsum"] + nbytes["gemm"])) < (FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3)
-    kern_name = {"einsum": "grouped_fp8_einsum", "gemm": "fp8_gemm_nt"}[dom]
+    dom = max(("einsum", "gemm"), key=lambda k: t_k[k])
+    t_dom = t_k[dom]
+    hbm_bound = (flops[dom] / nbytes[dom]) < (FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3)
+    kern_name = KERNEL_NAMES[dom]
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
     if os.path.exists(tpath):
@@ -336,14 +344,16 @@ def main():
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp8 (e4m3 x e4m3, fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": f"{args.config}: o_proj chain M={M} tokens, wo_a {G}x{K}->{N}, wo_b {G * N}->{P}",
+        "config": {"workload": f"{args.config}: o_proj chain (mxfp8_quantize -> grouped_fp8_einsum with MXFP8 "
+                               f"epilogue -> fp8_gemm_nt), M={M} tokens, wo_a {G}x{K}->{N}, wo_b {G * N}->{P}",
                    "M": M, "G": G, "K": K, "N": N, "P": P, "seed": cfg.seed,
                    "x": "BF16 N(0,1)" + (f", {cfg.outlier_rate:g} of entries x100" if cfg.outlier_rate else ""),
                    "weights": "MXFP8 of BF16 N(0,0.02)", "rotating_sets": R, "timing": "HIP graph replay"},
         "us_per_call": us,
         "arms_us_per_call": {a: r["us_per_call"] for a, r in results.items()},
-        "kernels_avg_us": {"grouped_fp8_einsum": t_einsum, "fp8_gemm_nt": t_gemm},
-        "hbm_roofline_frac_chain": (nbytes["einsum"] + nbytes["gemm"]) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "fusion_saving_us": (results["unfused"]["us_per_call"] - us) if "unfused" in results else None,
+        "kernels_avg_us": {KERNEL_NAMES[k]: v for k, v in t_k.items()},
+        "hbm_roofline_frac_chain": sum(nbytes.values()) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "mfma_roofline_frac_chain": value / FP8_PEAK_TFLOPS,
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),

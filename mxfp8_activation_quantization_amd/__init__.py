@@ -6,7 +6,7 @@ ctypes; torch supplies device memory and streams.
     mxfp8_quantize      BF16 -> E4M3 codes + packed UE8M0 scales (one per 32 elements)
     grouped_fp8_einsum  wo_a: grouped MXFP8 GEMM whose epilogue writes z as MXFP8 and/or BF16
     fp8_gemm_nt         wo_b: MXFP8 GEMM with 1x32 scale blocks on both operands, BF16 out
-    o_proj_chain        the three in sequence on one stream
+    o_proj_chain        the chain on one stream (modes: chain, x_fused, unfused)
 """
 from .binding import (  # noqa: F401
     CHAIN_MODES,

@@ -246,23 +246,25 @@ def fp8_gemm_nt(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_s
 
 # ----------------------------------------------------------------------------- chain
 
-CHAIN_MODES = ("fused", "prequant", "unfused")
+CHAIN_MODES = ("chain", "x_fused", "unfused")
 
 
 def o_proj_chain(x: torch.Tensor, wo_a: torch.Tensor, wo_a_sf: torch.Tensor, wo_b: torch.Tensor,
-                 wo_b_sf: torch.Tensor, mode: str = "fused", stream=None) -> torch.Tensor:
+                 wo_b_sf: torch.Tensor, mode: str = "chain", stream=None) -> torch.Tensor:
     """The o_proj chain on one stream, no host synchronization; returns BF16 [M, P].
 
-    mode "fused":    einsum quantizes BF16 x in its load path and writes MXFP8 z; GEMM consumes (z, sf).
-    mode "prequant": mxfp8_quantize(x), then the same einsum and GEMM (three launches).
-    mode "unfused":  mxfp8_quantize(x), einsum writes BF16 z, mxfp8_quantize(z), GEMM: the arrangement
-                     the fused epilogue replaces (vLLM PR #60118, Conversation).
+    mode "chain":   mxfp8_quantize(x); the einsum writes z as MXFP8 in its epilogue; the GEMM consumes
+                    (z, sf) as is (vLLM PR #60118, Overview: wo_a writes wo_b's MXFP8 input).
+    mode "x_fused": as "chain", but the einsum quantizes BF16 x in its own load path (two launches).
+    mode "unfused": the arrangement the fused epilogue replaces: the einsum writes BF16 z and a standalone
+                    mxfp8_quantize of z feeds the GEMM (PR #60118, Conversation).
+    All three give identical bytes.
     """
-    if mode == "fused":
-        z_q, z_sf = grouped_fp8_einsum(x, None, wo_a, wo_a_sf, out="mxfp8", stream=stream)
-    elif mode == "prequant":
+    if mode == "chain":
         x_q, x_sf = mxfp8_quantize(x, stream=stream)
         z_q, z_sf = grouped_fp8_einsum(x_q, x_sf, wo_a, wo_a_sf, out="mxfp8", stream=stream)
+    elif mode == "x_fused":
+        z_q, z_sf = grouped_fp8_einsum(x, None, wo_a, wo_a_sf, out="mxfp8", stream=stream)
     elif mode == "unfused":
         x_q, x_sf = mxfp8_quantize(x, stream=stream)
         z = grouped_fp8_einsum(x_q, x_sf, wo_a, wo_a_sf, out="bf16", stream=stream)

@@ -286,26 +286,26 @@ def test_chain_vs_oracle_and_modes_identical(lib, name):
     c = get_case(name, lib)
     ref = c.oracle()
     outs = {m: lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode=m) for m in lib.CHAIN_MODES}
-    again = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
-    assert torch.equal(outs["fused"], again)                 # deterministic
+    again = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="chain")
+    assert torch.equal(outs["chain"], again)                 # deterministic
     for m in lib.CHAIN_MODES:
-        assert torch.equal(outs[m], outs["fused"]), m
+        assert torch.equal(outs[m], outs["chain"]), m
     z_q, z_sf = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="mxfp8")
-    check_out_against_oracle(c, outs["fused"], z_q, z_sf, ref)
+    check_out_against_oracle(c, outs["chain"], z_q, z_sf, ref)
 
 
 @pytest.mark.parametrize("M", [1, 7, 33, 129, 300])
 def test_ragged_token_counts(lib, M):
     c = get_case("ragged", lib)
     x = c.x[:M]
-    out = lib.o_proj_chain(x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
+    out = lib.o_proj_chain(x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="chain")
     rows = list(range(M))
     ref = cr.o_proj_chain_rows(c.x_bits, *c.o_w, rows=rows)
     z_q, z_sf, z_b = lib.grouped_fp8_einsum(x, None, c.wa_q, c.wa_sf, out="both")
     check_z_against_oracle(z_q, z_sf, z_b, ref)
     check_out_against_oracle(c, out, z_q, z_sf, ref)
     # rows are independent: the first M rows of the 300-row batch give the same bytes
-    full = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
+    full = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="chain")
     assert torch.equal(full[:M], out)
 
 
@@ -329,7 +329,7 @@ def test_outputs_respect_strides_and_guards(lib):
 def test_large_configs_sampled_rows(lib, name):
     c = get_case(name, lib)
     M = c.shape.M
-    out = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="fused")
+    out = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="chain")
     z_q, z_sf, z_b = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.choice(M, 128, replace=False)]))
