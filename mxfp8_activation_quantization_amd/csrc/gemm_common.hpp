@@ -16,6 +16,8 @@
 // one 32-wide block of n for one token, shared with the partner lane l ^ 32.
 #pragma once
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "mx_device.hpp"
 
@@ -116,6 +118,38 @@ __device__ __forceinline__ void dl_load16(const Rsrc& r, const void* lds, int vo
 __device__ __forceinline__ void dl_load4(const Rsrc& r, const void* lds, int voff, int soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
+}
+
+// LDS reads with a constant offset (inline assembly: see the direct-to-LDS GEMM).
+// The result is not valid until a later s_waitcnt lgkmcnt(0) that the caller
+// ties to the result registers.
+template <int OFF>
+__device__ __forceinline__ v4i lds_read16(int addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS instruction offsets are 16 bits");
+  v4i v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+
+template <int OFF>
+__device__ __forceinline__ int lds_read4(int addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS instruction offsets are 16 bits");
+  int v;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+
+__device__ __forceinline__ v8i join8(const v4i& lo, const v4i& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 // s_waitcnt vmcnt(N) for a compile-time N.

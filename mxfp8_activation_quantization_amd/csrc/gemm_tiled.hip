@@ -300,12 +300,18 @@ __device__ __forceinline__ v8i dl_read_frag(const uint8_t* stage_op, int T, int 
   return frag(*reinterpret_cast<const uint4*>(b + 16 * (q ^ gi)), *reinterpret_cast<const uint4*>(b + 16 * ((2 + q) ^ gi)));
 }
 
+// LDS of the direct-to-LDS kernel: four stages of operand data, then four stages
+// of scale words.  A stage's data is 32 KB (256 + 256 rows x 64 bytes), so stages
+// 0-1 and 2-3 each fit one 64 KB window of the LDS instruction offset field: one
+// per-lane base address per window serves every fragment read.
 template <class C>
-struct DlStage {
-  uint8_t w[C::BN * 64];
-  uint8_t x[C::BM * 64];
-  uint32_t ws[C::BN];
-  uint32_t xs[C::BM];
+struct DlLds {
+  static constexpr int DATA = (C::BN + C::BM) * 64, SC = (C::BN + C::BM) * 4;
+  static constexpr int W = 0, X = C::BN * 64;              // within a stage's data
+  static constexpr int WS = 0, XS = C::BN * 4;             // within a stage's scales
+  static constexpr int SCALES = 4 * DATA;
+  static constexpr int BYTES = 4 * DATA + 4 * SC;
+  static_assert(2 * DATA <= 65536, "two stages per 64 KB window");
 };
 
 template <class C, int OUT>
@@ -317,7 +323,8 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   constexpr int L = WI + XI + 2;                 // + one scale-word load per operand
   // four separate stage buffers: the compiler can then tell a stage being filled
   // from the stage being read and inserts no waits of its own between them
-  __shared__ __attribute__((aligned(1024))) DlStage<C> st0, st1, st2, st3;
+  using Lds = DlLds<C>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds::BYTES];
 
   // the wave index is uniform: keep it in a scalar register (load offsets and LDS bases derive from it)
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 5, i = lane & 31;
@@ -340,39 +347,47 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   const int ldw = (int)p.K, ldx = (int)p.ld_x, ldxs = (int)(p.ld_xsf * 4);
   const Rsrc rw = make_rsrc_sgpr(p.w + ((int64_t)g * p.N + n0) * p.K, (int64_t)C::BN * p.K);
   const Rsrc rws = make_rsrc_sgpr(p.w_sf + ((int64_t)g * p.N + n0) * ksteps, (int64_t)C::BN * ksteps * 4);
-  // activation ranges end at token row m_rows (row starts only: see the offsets below)
-  const Rsrc rx = make_rsrc_sgpr(static_cast<const uint8_t*>(p.x) + m0 * ldx, m_rows * ldx);
-  const Rsrc rxs = make_rsrc_sgpr(p.x_sf + m0 * p.ld_xsf, m_rows * ldxs);
+  // Activations: every load instruction covers 16 token rows (64 for the scale
+  // words) and gets its own buffer resource starting at its first row and ending
+  // at row m_rows; the per-lane offset holds the row within the instruction, and
+  // the range check -- which sees the per-lane offset only -- turns rows past M
+  // into zeros without reading them.
   const int xcol0 = (int)((int64_t)g * p.K);
   const int xsfcol0 = g * ksteps * 4;
+  const uint8_t* x_tile = static_cast<const uint8_t*>(p.x) + m0 * ldx;
+  const int32_t* xsf_tile = p.x_sf + m0 * p.ld_xsf;
+  auto x_rsrc = [&](int row0) {
+    const int64_t rows = m_rows - row0;
+    return make_rsrc_sgpr(x_tile + (int64_t)row0 * ldx, rows > 0 ? rows * ldx : 0);
+  };
+  auto xs_rsrc = [&](int row0) {
+    const int64_t rows = m_rows - row0;
+    return make_rsrc_sgpr(xsf_tile + (int64_t)row0 * p.ld_xsf, rows > 0 ? rows * ldxs : 0);
+  };
 
-  // Per-lane parts of the load offsets.  Activation offsets carry the whole row
-  // part (row * ld) in the per-lane register -- the only part the range check
-  // sees -- and the column part (< ld) in the scalar offset, so a row at or past
-  // m_rows is out of range and loads zeros.
+  // per-lane parts of the load offsets (the same for every stage and instruction)
   const int lr = lane >> 2, lc = (lane & 3) ^ dl_g(lane >> 2);
-  const int vw = lr * ldw + lc * 16;
-  const int vws = lane * ksteps * 4;
-  int vx[XI];
-#pragma unroll
-  for (int j = 0; j < XI; ++j) vx[j] = (16 * (4 * j + wave) + lr) * ldx + lc * 16;
-  const int vxs = (64 * (wave % (C::BM / 64)) + lane) * ldxs;
+  const int vw = lr * ldw + lc * 16, vx = lr * ldx + lc * 16;
+  const int vws = lane * ksteps * 4, vxs = lane * ldxs;
 
-  auto issue = [&](DlStage<C>& S, int t) {
+  // stage buffer b (= t % 4) of stage t
+  auto issue = [&](int b, int t) {
+    uint8_t* data = smem + b * Lds::DATA;
+    uint8_t* sc = smem + Lds::SCALES + b * Lds::SC;
     const int kt = t >> 1, ks = t & 1;
 #pragma unroll
     for (int j = 0; j < WI; ++j) {
       const int n = 4 * j + wave;                 // rows 16n .. 16n+15
-      dl_load16(rw, S.w + n * 1024, vw, 16 * n * ldw + kt * 128 + ks * 64);
+      dl_load16(rw, data + Lds::W + n * 1024, vw, 16 * n * ldw + kt * 128 + ks * 64);
     }
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
       const int n = 4 * j + wave;
-      dl_load16(rx, S.x + n * 1024, vx[j], xcol0 + kt * 128 + ks * 64);
+      dl_load16(x_rsrc(16 * n), data + Lds::X + n * 1024, vx, xcol0 + kt * 128 + ks * 64);
     }
     const int jw = wave % (C::BN / 64), jx = wave % (C::BM / 64);
-    dl_load4(rws, S.ws + 64 * jw, vws, (64 * jw * ksteps + kt) * 4);
-    dl_load4(rxs, S.xs + 64 * jx, vxs, xsfcol0 + kt * 4);
+    dl_load4(rws, sc + Lds::WS + 256 * jw, vws, (64 * jw * ksteps + kt) * 4);
+    dl_load4(xs_rsrc(64 * jx), sc + Lds::XS + 256 * jx, vxs, xsfcol0 + kt * 4);
   };
 
   v16f acc[C::TN][C::TM];
@@ -381,60 +396,130 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
 #pragma unroll
     for (int b = 0; b < C::TM; ++b) acc[a][b] = zero16();
 
-  auto compute = [&](const DlStage<C>& S, auto ks_tag) {
-    constexpr int KS = decltype(ks_tag)::value;
-    int sw[C::TN], sx[C::TM];
+  // MFMA operands of one stage, held in registers: while the MFMAs of stage t run
+  // on one set, the LDS reads of stage t+1 fill the other.
+  struct Frags {
     v8i fw[C::TN], fx[C::TM];
+    int sw[C::TN], sx[C::TM];
+  };
+  // The fragment reads are inline assembly with explicit base registers and
+  // constant offsets: a handful of per-lane bases serve every stage and tile (left
+  // to itself the compiler keeps one address register per stage and tile, runs
+  // out of registers and spills -- and a spill reload in this loop would wait for
+  // every load in flight).  The compiler does not see these reads complete, so
+  // wait_frags() waits for them and ties the registers to that wait.
+  const int gi = dl_g(i);
+  const int off_lo = 64 * i + 16 * (q ^ gi), off_hi = 64 * i + 16 * ((2 + q) ^ gi);
+  const int base = (int)lds_addr(smem);
+  const int aw_lo = base + wn * C::TN * 2048 + off_lo, aw_hi = base + wn * C::TN * 2048 + off_hi;
+  const int ax_lo = base + wm * C::TM * 2048 + off_lo, ax_hi = base + wm * C::TM * 2048 + off_hi;
+  constexpr int WIN = 2 * Lds::DATA;              // stages 2-3 start here
+  const int aw_lo1 = aw_lo + WIN, aw_hi1 = aw_hi + WIN, ax_lo1 = ax_lo + WIN, ax_hi1 = ax_hi + WIN;
+  const int aws = base + Lds::SCALES + Lds::WS + (wn * C::TN * 32 + i) * 4;
+  const int axs = base + Lds::SCALES + Lds::XS + (wm * C::TM * 32 + i) * 4;
+  auto read = [&](auto buf_tag, Frags& F) {
+    constexpr int B = decltype(buf_tag)::value;
+    constexpr int D = (B & 1) * Lds::DATA;              // within the 64 KB window of stage B
+    const int wl = (B >> 1) ? aw_lo1 : aw_lo, wh = (B >> 1) ? aw_hi1 : aw_hi;
+    const int xl = (B >> 1) ? ax_lo1 : ax_lo, xh = (B >> 1) ? ax_hi1 : ax_hi;
+    static_for<C::TN>([&](auto a_tag) {
+      constexpr int a = decltype(a_tag)::value;
+      F.sw[a] = lds_read4<B * Lds::SC + a * 128>(aws);
+      F.fw[a] = join8(lds_read16<D + Lds::W + a * 2048>(wl), lds_read16<D + Lds::W + a * 2048>(wh));
+    });
+    static_for<C::TM>([&](auto c_tag) {
+      constexpr int c = decltype(c_tag)::value;
+      F.sx[c] = lds_read4<B * Lds::SC + c * 128>(axs);
+      F.fx[c] = join8(lds_read16<D + Lds::X + c * 2048>(xl), lds_read16<D + Lds::X + c * 2048>(xh));
+    });
+  };
+  auto wait_frags = [&](Frags& F) {
+    static_assert(C::TN == 4 && C::TM <= 4, "register ties below list four tiles per operand");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(F.fw[0]), "+v"(F.fw[1]), "+v"(F.fw[2]), "+v"(F.fw[3]), "+v"(F.sw[0]), "+v"(F.sw[1]),
+                   "+v"(F.sw[2]), "+v"(F.sw[3]));
+    if constexpr (C::TM == 4)
+      asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.fx[2]), "+v"(F.fx[3]), "+v"(F.sx[0]), "+v"(F.sx[1]),
+                   "+v"(F.sx[2]), "+v"(F.sx[3]));
+    else
+      asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.sx[0]), "+v"(F.sx[1]));
 #pragma unroll
-    for (int a = 0; a < C::TN; ++a) {
-      sw[a] = (int)(S.ws[(wn * C::TN + a) * 32 + i] >> (8 * q));
-      fw[a] = dl_read_frag(S.w, wn * C::TN + a, lane);
-    }
+    for (int a = 0; a < C::TN; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
 #pragma unroll
-    for (int b = 0; b < C::TM; ++b) {
-      sx[b] = (int)(S.xs[(wm * C::TM + b) * 32 + i] >> (8 * q));
-      fx[b] = dl_read_frag(S.x, wm * C::TM + b, lane);
-    }
+    for (int c = 0; c < C::TM; ++c) F.sx[c] = (int)((uint32_t)F.sx[c] >> (8 * q));
+  };
+  // half H (0, 1) of the TN x TM MFMAs of a stage
+  auto mma = [&](const Frags& F, auto ks_tag, auto half_tag) {
+    constexpr int KS = decltype(ks_tag)::value, H = decltype(half_tag)::value;
 #pragma unroll
-    for (int a = 0; a < C::TN; ++a)
+    for (int a = H * C::TN / 2; a < (H + 1) * C::TN / 2; ++a)
 #pragma unroll
-      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2 * KS>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
+      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2 * KS>(F.fw[a], F.fx[b], acc[a][b], F.sw[a], F.sx[b]);
   };
 
-  // Stage t lives in buffer t % 4.  Before stage t is read: this wave's loads of
-  // stage t are complete (at most the stages after it, up to t+2, still in
-  // flight: L loads each), then a barrier makes every wave's loads visible and
-  // guarantees that stage t-1's buffer is no longer read, so stage t+3 can be
-  // issued into it.
-  auto step = [&](DlStage<C>& cur, DlStage<C>& nxt3, int t, auto ks_tag) {
-    if (t + 2 < nst) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
-    else if (t + 1 < nst) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_barrier" ::: "memory");   // no LDS writes of its own: vmcnt above covers the DMA
-    if (t + 3 < nst) issue(nxt3, t + 3);
-    compute(cur, ks_tag);
+  // Stage t lives in buffer t % 4 and its operands in Frags t % 2.  One step:
+  // first half of stage t's MFMAs; then -- once this wave's loads of stage t+1 are
+  // complete (at most stages t+2, t+3 still in flight, L loads each) -- a barrier
+  // makes every wave's stage t+1 visible and, since every wave has consumed its
+  // stage-t operands by then, frees buffer t % 4 for the loads of stage t+4; the
+  // LDS reads of stage t+1 follow; last, the second half of stage t's MFMAs, which
+  // covers the LDS latency.
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  auto step = [&](Frags& cur, Frags& nxt, auto next_buf, int refill, int t, auto ks_tag) {
+    wait_frags(cur);
+    mma(cur, ks_tag, H0{});
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < nst) {
+      const int later = nst - 2 - t;
+      if (later >= 2) wait_vmcnt<2 * L>();
+      else if (later == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");
+      if (t + 4 < nst) issue(refill, t + 4);
+      read(next_buf, nxt);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(cur, ks_tag, H1{});
   };
 
-  issue(st0, 0);
-  if (nst > 1) issue(st1, 1);
-  if (nst > 2) issue(st2, 2);
-  using K0 = std::integral_constant<int, 0>;
-  using K1 = std::integral_constant<int, 1>;
+  Frags f0, f1;
+  issue(0, 0);
+  issue(1, 1);                                 // nst = 2 ksteps >= 2
+  if (nst > 2) issue(2, 2);
+  if (nst > 3) issue(3, 3);
+  if (nst > 3) wait_vmcnt<3 * L>();
+  else wait_vmcnt<L>();                          // nst == 2: stage 1 may still be in flight
+  asm volatile("s_barrier" ::: "memory");
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  read(B0{}, f0);
   for (int t = 0; t < nst; t += 4) {
-    step(st0, st3, t, K0{});
-    step(st1, st0, t + 1, K1{});              // nst is even: stage t + 1 always exists
+    step(f0, f1, B1{}, 0, t, B0{});            // (stage parity KS = t & 1 doubles as the opsel tag)
+    step(f1, f0, B2{}, 1, t + 1, B1{});        // nst is even: stage t + 1 always exists
     if (t + 2 < nst) {
-      step(st2, st1, t + 2, K0{});
-      step(st3, st2, t + 3, K1{});
+      step(f0, f1, B3{}, 2, t + 2, B0{});
+      step(f1, f0, B0{}, 3, t + 3, B1{});
     }
   }
 
+  // Epilogue one tile at a time (bounds the registers the accumulator copies
+  // need).  The lane's row i and half q are taken back from a base address that
+  // lives through the loop anyway, so that no separate register has to survive it.
+  int aw = aw_lo;
+  asm volatile("" : "+v"(aw));                     // opaque: keeps the compiler from reusing the original i
+  const int i_e = (aw - base - wn * C::TN * 2048) >> 6;
+  const int q_e = ((aw >> 4) & 3) ^ dl_g(i_e);
 #pragma unroll
   for (int b = 0; b < C::TM; ++b) {
-    const int64_t m = m0 + (wm * C::TM + b) * 32 + i;
+    const int64_t m = m0 + (wm * C::TM + b) * 32 + i_e;
 #pragma unroll
-    for (int a = 0; a < C::TN; ++a)
-      store_tile<OUT>(p, acc[a][b], m, m < p.M, (int64_t)g * p.N + n0 + (wn * C::TN + a) * 32, q);
+    for (int a = 0; a < C::TN; ++a) {
+      store_tile<OUT>(p, acc[a][b], m, m < p.M, (int64_t)g * p.N + n0 + (wn * C::TN + a) * 32, q_e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
