@@ -300,18 +300,23 @@ __device__ __forceinline__ v8i dl_read_frag(const uint8_t* stage_op, int T, int 
   return frag(*reinterpret_cast<const uint4*>(b + 16 * (q ^ gi)), *reinterpret_cast<const uint4*>(b + 16 * ((2 + q) ^ gi)));
 }
 
-// LDS of the direct-to-LDS kernel: four stages of operand data, then four stages
-// of scale words.  A stage's data is 32 KB (256 + 256 rows x 64 bytes), so stages
-// 0-1 and 2-3 each fit one 64 KB window of the LDS instruction offset field: one
-// per-lane base address per window serves every fragment read.
+// LDS of the direct-to-LDS kernel: four half-step stages of operand data, then
+// two buffers of scale words.  A scale buffer holds the words of four K-steps
+// (eight stages) for every row of both operands, 16 bytes per row, so the scale
+// loads touch each row once per four K-steps instead of once per stage: loads of
+// one word per row cost an L2 request per row, as many as the operand data.
+// Stages 0-1 and 2-3 each fit one 64 KB window of the LDS instruction offset
+// field, so one per-lane base address per window serves every fragment read.
 template <class C>
 struct DlLds {
-  static constexpr int DATA = (C::BN + C::BM) * 64, SC = (C::BN + C::BM) * 4;
+  static constexpr int DATA = (C::BN + C::BM) * 64;
   static constexpr int W = 0, X = C::BN * 64;              // within a stage's data
-  static constexpr int WS = 0, XS = C::BN * 4;             // within a stage's scales
+  static constexpr int SROWS = C::BN + C::BM;              // weight rows, then token rows
+  static constexpr int SBUF = SROWS * 16;
   static constexpr int SCALES = 4 * DATA;
-  static constexpr int BYTES = 4 * DATA + 4 * SC;
+  static constexpr int BYTES = 4 * DATA + 2 * SBUF;
   static_assert(2 * DATA <= 65536, "two stages per 64 KB window");
+  static_assert(BYTES <= 160 * 1024, "LDS of one CU");
 };
 
 template <class C, int OUT>
@@ -320,9 +325,8 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   static_assert(C::NW == 4, "four waves");
   constexpr int WI = C::BN / 64;                 // weight load instructions per wave and stage
   constexpr int XI = C::BM / 64;                 // activation load instructions per wave and stage
-  constexpr int L = WI + XI + 2;                 // + one scale-word load per operand
-  // four separate stage buffers: the compiler can then tell a stage being filled
-  // from the stage being read and inserts no waits of its own between them
+  constexpr int L = WI + XI;                     // loads per wave and stage
+  constexpr int SI = (C::BN + C::BM) / 64;       // scale-word load instructions per wave and scale group
   using Lds = DlLds<C>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds::BYTES];
 
@@ -341,17 +345,17 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   const int64_t n0 = (int64_t)nt * C::BN;
   const int64_t m0 = (int64_t)mt * C::BM;
   const int ksteps = (int)(p.K / 128);
-  const int nst = 2 * ksteps;
+  const int nst = 2 * ksteps;                    // half-step stages, 64 deep
   const int64_t rows_left = p.M - m0;
   const int64_t m_rows = rows_left < C::BM ? rows_left : C::BM;
   const int ldw = (int)p.K, ldx = (int)p.ld_x, ldxs = (int)(p.ld_xsf * 4);
   const Rsrc rw = make_rsrc_sgpr(p.w + ((int64_t)g * p.N + n0) * p.K, (int64_t)C::BN * p.K);
   const Rsrc rws = make_rsrc_sgpr(p.w_sf + ((int64_t)g * p.N + n0) * ksteps, (int64_t)C::BN * ksteps * 4);
-  // Activations: every load instruction covers 16 token rows (64 for the scale
-  // words) and gets its own buffer resource starting at its first row and ending
-  // at row m_rows; the per-lane offset holds the row within the instruction, and
-  // the range check -- which sees the per-lane offset only -- turns rows past M
-  // into zeros without reading them.
+  // Activations: every load instruction covers 16 token rows and gets its own
+  // buffer resource starting at its first row and ending at row m_rows; the
+  // per-lane offset holds the row within the instruction, and the range check --
+  // which sees the per-lane offset only -- turns rows past M into zeros without
+  // reading them.
   const int xcol0 = (int)((int64_t)g * p.K);
   const int xsfcol0 = g * ksteps * 4;
   const uint8_t* x_tile = static_cast<const uint8_t*>(p.x) + m0 * ldx;
@@ -368,12 +372,12 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   // per-lane parts of the load offsets (the same for every stage and instruction)
   const int lr = lane >> 2, lc = (lane & 3) ^ dl_g(lane >> 2);
   const int vw = lr * ldw + lc * 16, vx = lr * ldx + lc * 16;
-  const int vws = lane * ksteps * 4, vxs = lane * ldxs;
+  // scale words: lane l reads word l % 4 of the group's four in row l / 4 of the instruction's 16 rows
+  const int vws = lr * ksteps * 4 + (lane & 3) * 4, vxs = lr * ldxs + xsfcol0 + (lane & 3) * 4;
 
-  // stage buffer b (= t % 4) of stage t
+  // operand data of stage t into stage buffer b (= t % 4)
   auto issue = [&](int b, int t) {
     uint8_t* data = smem + b * Lds::DATA;
-    uint8_t* sc = smem + Lds::SCALES + b * Lds::SC;
     const int kt = t >> 1, ks = t & 1;
 #pragma unroll
     for (int j = 0; j < WI; ++j) {
@@ -385,9 +389,19 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
       const int n = 4 * j + wave;
       dl_load16(x_rsrc(16 * n), data + Lds::X + n * 1024, vx, xcol0 + kt * 128 + ks * 64);
     }
-    const int jw = wave % (C::BN / 64), jx = wave % (C::BM / 64);
-    dl_load4(rws, sc + Lds::WS + 256 * jw, vws, (64 * jw * ksteps + kt) * 4);
-    dl_load4(xs_rsrc(64 * jx), sc + Lds::XS + 256 * jx, vxs, xsfcol0 + kt * 4);
+  };
+  // scale words of group s (K-steps 4s .. 4s+3) into scale buffer s % 2.  Words
+  // past the end of a row (last group of a K range that is not a multiple of
+  // four steps) are never used; the whole offset is in voffset, so the range
+  // check also covers them.
+  auto issue_scales = [&](int s) {
+    uint8_t* sc = smem + Lds::SCALES + (s & 1) * Lds::SBUF;
+    static_for<SI>([&](auto j_tag) {
+      constexpr int j = decltype(j_tag)::value;
+      const int n = 4 * j + wave;                 // rows 16n .. 16n+15 of the weight-then-token row list
+      if constexpr (4 * j < C::BN / 16) dl_load4(rws, sc + n * 256, vws + 16 * n * ksteps * 4 + 16 * s, 0);
+      else dl_load4(xs_rsrc(16 * n - C::BN), sc + n * 256, vxs + 16 * s, 0);
+    });
   };
 
   v16f acc[C::TN][C::TM];
@@ -411,25 +425,27 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   const int gi = dl_g(i);
   const int off_lo = 64 * i + 16 * (q ^ gi), off_hi = 64 * i + 16 * ((2 + q) ^ gi);
   const int base = (int)lds_addr(smem);
+  constexpr int WIN = 2 * Lds::DATA;              // stages 2-3 start here
   const int aw_lo = base + wn * C::TN * 2048 + off_lo, aw_hi = base + wn * C::TN * 2048 + off_hi;
   const int ax_lo = base + wm * C::TM * 2048 + off_lo, ax_hi = base + wm * C::TM * 2048 + off_hi;
-  constexpr int WIN = 2 * Lds::DATA;              // stages 2-3 start here
   const int aw_lo1 = aw_lo + WIN, aw_hi1 = aw_hi + WIN, ax_lo1 = ax_lo + WIN, ax_hi1 = ax_hi + WIN;
-  const int aws = base + Lds::SCALES + Lds::WS + (wn * C::TN * 32 + i) * 4;
-  const int axs = base + Lds::SCALES + Lds::XS + (wm * C::TM * 32 + i) * 4;
-  auto read = [&](auto buf_tag, Frags& F) {
-    constexpr int B = decltype(buf_tag)::value;
-    constexpr int D = (B & 1) * Lds::DATA;              // within the 64 KB window of stage B
+  const int aws = base + Lds::SCALES + (wn * C::TN * 32 + i) * 16;
+  const int axs = base + Lds::SCALES + (C::BN + wm * C::TM * 32 + i) * 16;
+  // stage J (mod 16) of the unrolled loop: data buffer J % 4, scale buffer J / 8, scale word (J % 8) / 2
+  auto read = [&](auto stage_tag, Frags& F) {
+    constexpr int J = decltype(stage_tag)::value;
+    constexpr int B = J % 4, SB = (J / 8) * Lds::SBUF + ((J % 8) / 2) * 4;
+    constexpr int D = (B & 1) * Lds::DATA;              // within the 64 KB window of stage buffer B
     const int wl = (B >> 1) ? aw_lo1 : aw_lo, wh = (B >> 1) ? aw_hi1 : aw_hi;
     const int xl = (B >> 1) ? ax_lo1 : ax_lo, xh = (B >> 1) ? ax_hi1 : ax_hi;
     static_for<C::TN>([&](auto a_tag) {
       constexpr int a = decltype(a_tag)::value;
-      F.sw[a] = lds_read4<B * Lds::SC + a * 128>(aws);
+      F.sw[a] = lds_read4<SB + a * 512>(aws);
       F.fw[a] = join8(lds_read16<D + Lds::W + a * 2048>(wl), lds_read16<D + Lds::W + a * 2048>(wh));
     });
     static_for<C::TM>([&](auto c_tag) {
       constexpr int c = decltype(c_tag)::value;
-      F.sx[c] = lds_read4<B * Lds::SC + c * 128>(axs);
+      F.sx[c] = lds_read4<SB + c * 512>(axs);
       F.fx[c] = join8(lds_read16<D + Lds::X + c * 2048>(xl), lds_read16<D + Lds::X + c * 2048>(xh));
     });
   };
@@ -448,7 +464,7 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
 #pragma unroll
     for (int c = 0; c < C::TM; ++c) F.sx[c] = (int)((uint32_t)F.sx[c] >> (8 * q));
   };
-  // half H (0, 1) of the TN x TM MFMAs of a stage
+  // half H (0, 1) of the TN x TM MFMAs of a stage; KS = stage parity (which 64 bytes of the K-step)
   auto mma = [&](const Frags& F, auto ks_tag, auto half_tag) {
     constexpr int KS = decltype(ks_tag)::value, H = decltype(half_tag)::value;
 #pragma unroll
@@ -457,33 +473,47 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
       for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2 * KS>(F.fw[a], F.fx[b], acc[a][b], F.sw[a], F.sx[b]);
   };
 
-  // Stage t lives in buffer t % 4 and its operands in Frags t % 2.  One step:
-  // first half of stage t's MFMAs; then -- once this wave's loads of stage t+1 are
-  // complete (at most stages t+2, t+3 still in flight, L loads each) -- a barrier
-  // makes every wave's stage t+1 visible and, since every wave has consumed its
-  // stage-t operands by then, frees buffer t % 4 for the loads of stage t+4; the
-  // LDS reads of stage t+1 follow; last, the second half of stage t's MFMAs, which
-  // covers the LDS latency.
+  // Stage t lives in data buffer t % 4, its scale words in scale buffer (t / 8) % 2,
+  // and its operands in Frags t % 2.  One step: first half of stage t's MFMAs; then
+  // -- once this wave's loads of stage t+1 are complete (stages t+2, t+3 may still
+  // be in flight) -- a barrier makes every wave's stage t+1 visible and, since
+  // every wave has consumed its stage-t operands by then, frees data buffer t % 4
+  // for the loads of stage t+4 (and, at t = 8s, scale buffer (s+1) % 2, last used
+  // by stages up to 8s-1, for scale group s+1); the LDS reads of stage t+1 follow;
+  // last, the second half of stage t's MFMAs, which covers the LDS latency.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
-  auto step = [&](Frags& cur, Frags& nxt, auto next_buf, int refill, int t, auto ks_tag) {
+  auto step = [&](Frags& cur, Frags& nxt, auto stage_tag, int t) {
+    constexpr int J = decltype(stage_tag)::value;     // t % 16
     wait_frags(cur);
-    mma(cur, ks_tag, H0{});
+    mma(cur, std::integral_constant<int, J & 1>{}, H0{});
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < nst) {
+      // loads issued after stage t+1's: stages t+2 and t+3 (L each), plus the
+      // scale group that rides with stage 8s+4 when that is one of them
       const int later = nst - 2 - t;
-      if (later >= 2) wait_vmcnt<2 * L>();
-      else if (later == 1) wait_vmcnt<L>();
-      else wait_vmcnt<0>();
+      const bool scales_later = (J % 8 == 1 || J % 8 == 2) && 8 * (t / 8 + 1) < nst;
+      if (later >= 2) {
+        if (scales_later) wait_vmcnt<2 * L + SI>();
+        else wait_vmcnt<2 * L>();
+      } else if (later == 1) {
+        wait_vmcnt<L>();                            // (nst is even: no scale group rides with stage t+2 here)
+      } else {
+        wait_vmcnt<0>();
+      }
       asm volatile("s_barrier" ::: "memory");
-      if (t + 4 < nst) issue(refill, t + 4);
-      read(next_buf, nxt);
+      if (t + 4 < nst) {
+        if (J % 8 == 0 && 8 * (t / 8 + 1) < nst) issue_scales(t / 8 + 1);
+        issue(J % 4, t + 4);
+      }
+      read(std::integral_constant<int, (J + 1) % 16>{}, nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mma(cur, ks_tag, H1{});
+    mma(cur, std::integral_constant<int, J & 1>{}, H1{});
   };
 
   Frags f0, f1;
+  issue_scales(0);
   issue(0, 0);
   issue(1, 1);                                 // nst = 2 ksteps >= 2
   if (nst > 2) issue(2, 2);
@@ -491,18 +521,15 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   if (nst > 3) wait_vmcnt<3 * L>();
   else wait_vmcnt<L>();                          // nst == 2: stage 1 may still be in flight
   asm volatile("s_barrier" ::: "memory");
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
-  using B3 = std::integral_constant<int, 3>;
-  read(B0{}, f0);
-  for (int t = 0; t < nst; t += 4) {
-    step(f0, f1, B1{}, 0, t, B0{});            // (stage parity KS = t & 1 doubles as the opsel tag)
-    step(f1, f0, B2{}, 1, t + 1, B1{});        // nst is even: stage t + 1 always exists
-    if (t + 2 < nst) {
-      step(f0, f1, B3{}, 2, t + 2, B0{});
-      step(f1, f0, B0{}, 3, t + 3, B1{});
-    }
+  read(std::integral_constant<int, 0>{}, f0);
+  for (int t0 = 0; t0 < nst; t0 += 16) {
+    static_for<8>([&](auto pair_tag) {           // stages come in pairs: nst is even
+      constexpr int P = decltype(pair_tag)::value;
+      if (P == 0 || t0 + 2 * P < nst) {
+        step(f0, f1, std::integral_constant<int, 2 * P>{}, t0 + 2 * P);
+        step(f1, f0, std::integral_constant<int, 2 * P + 1>{}, t0 + 2 * P + 1);
+      }
+    });
   }
 
   // Epilogue one tile at a time (bounds the registers the accumulator copies
