@@ -84,6 +84,88 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f& acc, i
   }
 }
 
+// Epilogue through LDS.  store_tile() above writes straight from the MFMA
+// layout, where a lane holds 16 columns of one token scattered over the tile: each
+// store instruction then touches 32 token rows with 8 (BF16) or 4 (E4M3) bytes
+// each.  Large tiles instead pass a wave's TN x 32 columns of 32 tokens through
+// LDS as BF16, token-major, and read them back along token rows, so that every
+// store writes 16 contiguous bytes per lane and whole 128-byte row segments per
+// group of lanes.  The arithmetic is the same as store_tile's (BF16 rounding,
+// block amax of the rounded values, scale exponent, encoding), so both give the
+// same bits.
+//
+// Row stride in LDS: TN * 64 bytes of BF16 plus 16 bytes of padding, which keeps
+// the 16-byte row reads aligned and spreads the 32 token rows of a write over
+// the banks.
+template <int TN>
+struct EpiLds {
+  static constexpr int RS = TN * 64 + 16;
+  static constexpr int BYTES = 32 * RS;
+};
+
+// Tile a (columns 32a .. 32a+31) of the wave's row block: lane (i, q) holds
+// token i, columns 8 r4 + 4 q + (0..3) for r4 = 0..3.
+template <int TN>
+__device__ __forceinline__ void epi_write_tile(uint8_t* chunk, const v16f& acc, int a, int i, int q) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const uint2 v = make_uint2(bf16_rne(acc[4 * r4]) | (bf16_rne(acc[4 * r4 + 1]) << 16),
+                               bf16_rne(acc[4 * r4 + 2]) | (bf16_rne(acc[4 * r4 + 3]) << 16));
+    *reinterpret_cast<uint2*>(chunk + i * EpiLds<TN>::RS + (a * 32 + 8 * r4 + 4 * q) * 2) = v;
+  }
+}
+
+// Stores the 32 tokens m_base .. m_base+31 (those below M) x TN * 32 columns from
+// column nb of the output row.  Call after every lane's epi_write_tile of the
+// block and a wait for those LDS writes.
+template <int OUT, int TN>
+__device__ __forceinline__ void epi_store_rows(const GemmArgs& p, const uint8_t* chunk, int64_t m_base, int64_t nb,
+                                               int lane) {
+  constexpr int RS = EpiLds<TN>::RS;
+  static_assert(TN == 1 || TN == 2 || TN == 4, "lane split of a row");
+  if constexpr (OUT & OUT_BF16) {
+    constexpr int LPR = 4 * TN, RPP = 64 / LPR;      // lanes per row (8 columns each), rows per pass
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int row = lane / LPR + pass * RPP, c8 = lane % LPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(chunk + row * RS + c8 * 16);
+      const int64_t m = m_base + row;
+      if (m < p.M) *reinterpret_cast<uint4*>(p.zb + m * p.ld_zb + nb + c8 * 8) = v;
+      __builtin_amdgcn_sched_barrier(0);            // one pass at a time: bounds the registers
+    }
+  }
+  if constexpr (OUT & OUT_MX) {
+    constexpr int RPP = 64 / TN;                       // one lane per 32-column block
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int row = lane / TN + pass * RPP, blk = lane % TN;
+      const uint4* src = reinterpret_cast<const uint4*>(chunk + row * RS + blk * 64);
+      uint32_t w[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 v = src[k];
+        w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) am = max(am, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+      const int e = scale_exp_from_amax(am);
+      const float scale = exp2_int(e);
+      uint32_t c[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c[k] = encode4(w[2 * k], w[2 * k + 1], scale);
+      const int64_t m = m_base + row;
+      if (m < p.M) {
+        uint8_t* dst = p.zq + m * p.ld_zq + nb + blk * 32;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(c[0], c[1], c[2], c[3]);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(c[4], c[5], c[6], c[7]);
+        p.zsf[m * p.ld_zsf_bytes + nb / 32 + blk] = (uint8_t)(e + 127);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kRawBufferFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked

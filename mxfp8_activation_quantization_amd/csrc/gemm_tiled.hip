@@ -351,6 +351,7 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   const int ldw = (int)p.K, ldx = (int)p.ld_x, ldxs = (int)(p.ld_xsf * 4);
   const Rsrc rw = make_rsrc_sgpr(p.w + ((int64_t)g * p.N + n0) * p.K, (int64_t)C::BN * p.K);
   const Rsrc rws = make_rsrc_sgpr(p.w_sf + ((int64_t)g * p.N + n0) * ksteps, (int64_t)C::BN * ksteps * 4);
+  const Rsrc rnull = make_rsrc_sgpr(p.w, 0);
   // Activations: every load instruction covers 16 token rows and gets its own
   // buffer resource starting at its first row and ending at row m_rows; the
   // per-lane offset holds the row within the instruction, and the range check --
@@ -375,32 +376,34 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   // scale words: lane l reads word l % 4 of the group's four in row l / 4 of the instruction's 16 rows
   const int vws = lr * ksteps * 4 + (lane & 3) * 4, vxs = lr * ldxs + xsfcol0 + (lane & 3) * 4;
 
-  // operand data of stage t into stage buffer b (= t % 4)
-  auto issue = [&](int b, int t) {
+  // Load instruction d (< WI: weights, then tokens) of stage t into stage buffer
+  // b (= t % 4).  With `on` false the instruction gets a resource of zero bytes:
+  // every lane is out of range, nothing is read and the buffer receives zeros --
+  // a no-op for a buffer nobody reads, issued without a branch.
+  auto issue_one = [&](auto d_tag, int b, int t, bool on) {
+    constexpr int d = decltype(d_tag)::value;
     uint8_t* data = smem + b * Lds::DATA;
     const int kt = t >> 1, ks = t & 1;
-#pragma unroll
-    for (int j = 0; j < WI; ++j) {
-      const int n = 4 * j + wave;                 // rows 16n .. 16n+15
-      dl_load16(rw, data + Lds::W + n * 1024, vw, 16 * n * ldw + kt * 128 + ks * 64);
-    }
-#pragma unroll
-    for (int j = 0; j < XI; ++j) {
-      const int n = 4 * j + wave;
-      dl_load16(x_rsrc(16 * n), data + Lds::X + n * 1024, vx, xcol0 + kt * 128 + ks * 64);
+    if constexpr (d < WI) {
+      const int n = 4 * d + wave;                 // rows 16n .. 16n+15
+      dl_load16(on ? rw : rnull, data + Lds::W + n * 1024, vw, 16 * n * ldw + kt * 128 + ks * 64);
+    } else {
+      const int n = 4 * (d - WI) + wave;
+      dl_load16(on ? x_rsrc(16 * n) : rnull, data + Lds::X + n * 1024, vx, xcol0 + kt * 128 + ks * 64);
     }
   };
+  auto issue = [&](int b, int t) { static_for<L>([&](auto d_tag) { issue_one(d_tag, b, t, t < nst); }); };
   // scale words of group s (K-steps 4s .. 4s+3) into scale buffer s % 2.  Words
   // past the end of a row (last group of a K range that is not a multiple of
   // four steps) are never used; the whole offset is in voffset, so the range
-  // check also covers them.
-  auto issue_scales = [&](int s) {
+  // check also covers them.  With `on` false: zero-byte resources, as above.
+  auto issue_scales = [&](int s, bool on) {
     uint8_t* sc = smem + Lds::SCALES + (s & 1) * Lds::SBUF;
     static_for<SI>([&](auto j_tag) {
       constexpr int j = decltype(j_tag)::value;
       const int n = 4 * j + wave;                 // rows 16n .. 16n+15 of the weight-then-token row list
-      if constexpr (4 * j < C::BN / 16) dl_load4(rws, sc + n * 256, vws + 16 * n * ksteps * 4 + 16 * s, 0);
-      else dl_load4(xs_rsrc(16 * n - C::BN), sc + n * 256, vxs + 16 * s, 0);
+      if constexpr (4 * j < C::BN / 16) dl_load4(on ? rws : rnull, sc + n * 256, vws + 16 * n * ksteps * 4 + 16 * s, 0);
+      else dl_load4(on ? xs_rsrc(16 * n - C::BN) : rnull, sc + n * 256, vxs + 16 * s, 0);
     });
   };
 
@@ -431,23 +434,26 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   const int aw_lo1 = aw_lo + WIN, aw_hi1 = aw_hi + WIN, ax_lo1 = ax_lo + WIN, ax_hi1 = ax_hi + WIN;
   const int aws = base + Lds::SCALES + (wn * C::TN * 32 + i) * 16;
   const int axs = base + Lds::SCALES + (C::BN + wm * C::TM * 32 + i) * 16;
-  // stage J (mod 16) of the unrolled loop: data buffer J % 4, scale buffer J / 8, scale word (J % 8) / 2
-  auto read = [&](auto stage_tag, Frags& F) {
-    constexpr int J = decltype(stage_tag)::value;
+  // Fragment read r of stage J (mod 16) of the unrolled loop: r < TN is weight
+  // tile r, then token tile r - TN; each is a scale word and two 16-byte halves.
+  // Stage J lives in data buffer J % 4 and scale buffer J / 8, scale word (J % 8) / 2.
+  auto read_tile = [&](auto r_tag, auto stage_tag, Frags& F) {
+    constexpr int r = decltype(r_tag)::value, J = decltype(stage_tag)::value;
     constexpr int B = J % 4, SB = (J / 8) * Lds::SBUF + ((J % 8) / 2) * 4;
     constexpr int D = (B & 1) * Lds::DATA;              // within the 64 KB window of stage buffer B
-    const int wl = (B >> 1) ? aw_lo1 : aw_lo, wh = (B >> 1) ? aw_hi1 : aw_hi;
-    const int xl = (B >> 1) ? ax_lo1 : ax_lo, xh = (B >> 1) ? ax_hi1 : ax_hi;
-    static_for<C::TN>([&](auto a_tag) {
-      constexpr int a = decltype(a_tag)::value;
-      F.sw[a] = lds_read4<SB + a * 512>(aws);
-      F.fw[a] = join8(lds_read16<D + Lds::W + a * 2048>(wl), lds_read16<D + Lds::W + a * 2048>(wh));
-    });
-    static_for<C::TM>([&](auto c_tag) {
-      constexpr int c = decltype(c_tag)::value;
+    if constexpr (r < C::TN) {
+      const int wl = (B >> 1) ? aw_lo1 : aw_lo, wh = (B >> 1) ? aw_hi1 : aw_hi;
+      F.sw[r] = lds_read4<SB + r * 512>(aws);
+      F.fw[r] = join8(lds_read16<D + Lds::W + r * 2048>(wl), lds_read16<D + Lds::W + r * 2048>(wh));
+    } else {
+      constexpr int c = r - C::TN;
+      const int xl = (B >> 1) ? ax_lo1 : ax_lo, xh = (B >> 1) ? ax_hi1 : ax_hi;
       F.sx[c] = lds_read4<SB + c * 512>(axs);
       F.fx[c] = join8(lds_read16<D + Lds::X + c * 2048>(xl), lds_read16<D + Lds::X + c * 2048>(xh));
-    });
+    }
+  };
+  auto read = [&](auto stage_tag, Frags& F) {
+    static_for<C::TN + C::TM>([&](auto r_tag) { read_tile(r_tag, stage_tag, F); });
   };
   auto wait_frags = [&](Frags& F) {
     static_assert(C::TN == 4 && C::TM <= 4, "register ties below list four tiles per operand");
@@ -479,47 +485,57 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   // be in flight) -- a barrier makes every wave's stage t+1 visible and, since
   // every wave has consumed its stage-t operands by then, frees data buffer t % 4
   // for the loads of stage t+4 (and, at t = 8s, scale buffer (s+1) % 2, last used
-  // by stages up to 8s-1, for scale group s+1); the LDS reads of stage t+1 follow;
-  // last, the second half of stage t's MFMAs, which covers the LDS latency.
+  // by stages up to 8s-1, for scale group s+1).  The second half of stage t's
+  // MFMAs follows, with the LDS reads of stage t+1 and the loads of stage t+4
+  // slotted between them: a wave issues in order, so a load instruction that has
+  // to wait for the memory pipeline then holds up at most one MFMA's worth of
+  // issue, not a whole half-stage.
+  //
+  // A step has no branches: a branch would split the scheduling region and let
+  // the compiler regroup the MFMAs.  Every step issues the loads of stage t+4 and,
+  // at t = 8s, of scale group s+1 -- switched off (zero-byte resources) where
+  // those do not exist -- so the number of loads issued after stage t+1's is the
+  // same constant at every step, and the last step's reads fetch a buffer that
+  // is never used.
   using H0 = std::integral_constant<int, 0>;
-  using H1 = std::integral_constant<int, 1>;
+  constexpr int NMF = C::TN / 2 * C::TM;             // MFMAs per half-stage
+  static_assert(C::TN + C::TM == L, "one fragment read per load instruction");
+  constexpr int PER = (2 * L + NMF - 1) / NMF;       // reads and loads slotted after each MFMA
   auto step = [&](Frags& cur, Frags& nxt, auto stage_tag, int t) {
     constexpr int J = decltype(stage_tag)::value;     // t % 16
+    constexpr int KS = J & 1;
     wait_frags(cur);
-    mma(cur, std::integral_constant<int, J & 1>{}, H0{});
+    mma(cur, std::integral_constant<int, KS>{}, H0{});
     __builtin_amdgcn_sched_barrier(0);
-    if (t + 1 < nst) {
-      // loads issued after stage t+1's: stages t+2 and t+3 (L each), plus the
-      // scale group that rides with stage 8s+4 when that is one of them
-      const int later = nst - 2 - t;
-      const bool scales_later = (J % 8 == 1 || J % 8 == 2) && 8 * (t / 8 + 1) < nst;
-      if (later >= 2) {
-        if (scales_later) wait_vmcnt<2 * L + SI>();
-        else wait_vmcnt<2 * L>();
-      } else if (later == 1) {
-        wait_vmcnt<L>();                            // (nst is even: no scale group rides with stage t+2 here)
-      } else {
-        wait_vmcnt<0>();
-      }
-      asm volatile("s_barrier" ::: "memory");
-      if (t + 4 < nst) {
-        if (J % 8 == 0 && 8 * (t / 8 + 1) < nst) issue_scales(t / 8 + 1);
-        issue(J % 4, t + 4);
-      }
-      read(std::integral_constant<int, (J + 1) % 16>{}, nxt);
-    }
+    // loads issued after stage t+1's: stages t+2 and t+3, plus scale group s+1
+    // when it went out with stage 8s+4, one of those two
+    wait_vmcnt<2 * L + ((J % 8 == 1 || J % 8 == 2) ? SI : 0)>();
+    asm volatile("s_barrier" ::: "memory");
+    if constexpr (J % 8 == 0) issue_scales(t / 8 + 1, 8 * (t / 8 + 1) < nst);
+    const bool refill = t + 4 < nst;
     __builtin_amdgcn_sched_barrier(0);
-    mma(cur, std::integral_constant<int, J & 1>{}, H1{});
+    static_for<NMF>([&](auto m_tag) {
+      constexpr int m = decltype(m_tag)::value;
+      constexpr int a = C::TN / 2 + m / C::TM, b = m % C::TM;
+      acc[a][b] = mfma_scaled<2 * KS>(cur.fw[a], cur.fx[b], acc[a][b], cur.sw[a], cur.sx[b]);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<PER>([&](auto k_tag) {
+        constexpr int o = m * PER + decltype(k_tag)::value;   // even: read o/2, odd: load o/2
+        if constexpr (o < 2 * L) {
+          if constexpr (o % 2 == 0)
+            read_tile(std::integral_constant<int, o / 2>{}, std::integral_constant<int, (J + 1) % 16>{}, nxt);
+          else
+            issue_one(std::integral_constant<int, o / 2>{}, J % 4, t + 4, refill);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   Frags f0, f1;
-  issue_scales(0);
-  issue(0, 0);
-  issue(1, 1);                                 // nst = 2 ksteps >= 2
-  if (nst > 2) issue(2, 2);
-  if (nst > 3) issue(3, 3);
-  if (nst > 3) wait_vmcnt<3 * L>();
-  else wait_vmcnt<L>();                          // nst == 2: stage 1 may still be in flight
+  issue_scales(0, true);
+  static_for<4>([&](auto b_tag) { issue(decltype(b_tag)::value, decltype(b_tag)::value); });   // off past nst
+  wait_vmcnt<3 * L>();
   asm volatile("s_barrier" ::: "memory");
   read(std::integral_constant<int, 0>{}, f0);
   for (int t0 = 0; t0 < nst; t0 += 16) {
@@ -532,21 +548,27 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
     });
   }
 
-  // Epilogue one tile at a time (bounds the registers the accumulator copies
-  // need).  The lane's row i and half q are taken back from a base address that
-  // lives through the loop anyway, so that no separate register has to survive it.
+  // Epilogue through LDS, one 32-token block at a time.  Every wave has waited
+  // for its last fragment reads before this barrier, so the stage buffers are free.
+  // The lane's row i and half q (and so the lane index) are taken back from a base
+  // address that lives through the loop anyway, so that nothing the epilogue
+  // derives from them is computed early and kept alive across the loop.
+  __syncthreads();
   int aw = aw_lo;
   asm volatile("" : "+v"(aw));                     // opaque: keeps the compiler from reusing the original i
   const int i_e = (aw - base - wn * C::TN * 2048) >> 6;
   const int q_e = ((aw >> 4) & 3) ^ dl_g(i_e);
+  static_assert(4 * EpiLds<C::TN>::BYTES <= Lds::BYTES, "epilogue blocks of the four waves");
+  uint8_t* chunk = smem + wave * EpiLds<C::TN>::BYTES;
+  const int64_t nb = (int64_t)g * p.N + n0 + wn * C::TN * 32;
 #pragma unroll
   for (int b = 0; b < C::TM; ++b) {
-    const int64_t m = m0 + (wm * C::TM + b) * 32 + i_e;
 #pragma unroll
     for (int a = 0; a < C::TN; ++a) {
-      store_tile<OUT>(p, acc[a][b], m, m < p.M, (int64_t)g * p.N + n0 + (wn * C::TN + a) * 32, q_e);
+      epi_write_tile<C::TN>(chunk, acc[a][b], a, i_e, q_e);
       __builtin_amdgcn_sched_barrier(0);
     }
+    epi_store_rows<OUT, C::TN>(p, chunk, m0 + (wm * C::TM + b) * 32, nb, i_e + 32 * q_e);
   }
 }
 
