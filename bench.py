@@ -16,7 +16,9 @@ reports the arm whose einsum quantizes BF16 x in its load path ("x_fused", two
 launches) and the unfused arm ("unfused": BF16 z re-quantized by a separate
 launch, the arrangement the fused epilogue replaces), per-kernel durations from
 HIP events on the launch stream, the dominant kernel's roofline fraction, and the
-CPU oracle timed on this host's cores.
+CPU oracle timed on this host's cores.  Per-kernel durations come from graphs of
+one kernel each, replayed back to back, so they compare with a profiler's kernel
+trace of the same command.
 """
 from __future__ import annotations
 
@@ -299,17 +301,33 @@ def main():
         print(f"[bench] arm {arm}: {ms_ev * 1e3:.2f} us/call (graph replay)", file=sys.stderr, flush=True)
         del graphs
 
-    # per-kernel durations: HIP events on the launch stream around each kernel of the headline chain
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            launch_chain(sets[i % R])
+    # Per-kernel durations: each launch of the headline chain captured alone in graphs
+    # (one launch per rotating set, so inputs stay cold), replayed back to back and
+    # timed with HIP events on the launch stream -- the kernel's own duration plus
+    # the small gap between graph nodes, comparable with a profiler's kernel trace.
+    def launch_one(kind, s):
+        if kind == "quantize":
+            L.mxfp8_quantize(s["x"], q=s["x_q"], sf=s["x_sf"], stream=stream)
+        elif kind == "einsum":
+            L.grouped_fp8_einsum(s["x_q"], s["x_sf"], s["wa_q"], s["wa_sf"], out="mxfp8", z_q=s["z_q"],
+                                 z_sf=s["z_sf"], stream=stream)
+        else:
+            L.fp8_gemm_nt(s["z_q"], s["z_sf"], s["wb_q"], s["wb_sf"], d=s["out"], stream=stream)
+
+    t_k = {}
+    for kind in ("quantize", "einsum", "gemm"):
+        graphs = []
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                launch_one(kind, s)
+                stream.synchronize()
+                with torch.cuda.graph(g, stream=stream):
+                    launch_one(kind, s)
+            graphs.append(g)
         torch.cuda.synchronize()
-        for i in range(args.steps):
-            launch_chain(sets[i % R], evs[i])
-    torch.cuda.synchronize()
-    t_k = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
-           for j, k in enumerate(("quantize", "einsum", "gemm"))}
+        t_k[kind] = time_arm_graphs(torch, graphs, stream, args.steps, args.warmup)
+        del graphs
 
     flops = chain_flops(M, G, K, N, P)
     nbytes = chain_bytes(M, G, K, N, P)

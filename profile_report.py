@@ -1,0 +1,153 @@
+"""Summaries of rocprofv3 output for profiles/.
+
+    python profile_report.py kernels DB.db [--title T] [--command C]
+        Markdown table of a kernel trace (the rocpd SQLite file rocprofv3 writes):
+        per kernel and grid, calls and average / min / max duration.
+
+    python profile_report.py traffic --config NAME --fetch F.csv --write W.csv \
+            --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N [--command C ...]
+        HBM bytes per launch of each kernel of the o_proj chain from two counter
+        runs (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch), each scaled by what
+        the same counter reads for a plain device copy of N bytes.  Writes
+        profiles/traffic_NAME.json (read by bench.py for roofline.traffic while
+        the kernel sources are unchanged) and prints a Markdown summary.
+
+Kernels are told apart by name and output mode: the direct-to-LDS and
+streaming GEMM kernels carry their output mode as the last template argument
+(1 = BF16 out: fp8_gemm_nt, 2 = MXFP8 out: grouped_fp8_einsum); the quantize
+kernel is mxfp8_quantize.  Only the grid that occurs most often is kept for
+each, which drops the one-off launches of the set-up (weight quantization).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import os
+import re
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def short_name(name: str) -> str:
+    s = re.sub(r"\(.*", "", name)
+    return s.replace("void mx::", "").replace("mx::", "").strip()
+
+
+def chain_role(name: str):
+    n = short_name(name)
+    if n.startswith("quantize_kernel"):
+        return "quantize"
+    m = re.match(r"(dl_gemm_kernel|big_gemm_kernel|stream_kernel|splitk_kernel)<(.*)>$", n)
+    if not m:
+        return None
+    out = m.group(2).split(",")[-1].strip()
+    return {"1": "gemm", "2": "einsum", "3": "einsum"}.get(out)
+
+
+def cmd_kernels(a):
+    db = sqlite3.connect(a.db)
+    rows = db.execute(
+        "select name, count(*), avg(duration), min(duration), max(duration), sum(duration), grid_x, workgroup_x, "
+        "vgpr_count, accum_vgpr_count, lds_size from kernels group by name, grid_x order by sum(duration) desc"
+    ).fetchall()
+    tot = sum(r[5] for r in rows) or 1
+    if a.title:
+        print(f"# {a.title}\n")
+    if a.command:
+        print("Command (from the repository root, one MI355X):\n\n    " + a.command + "\n")
+    print("| kernel | grid threads / WG | calls | avg µs | min µs | max µs | share | VGPR/AGPR | LDS B |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, n, avg, mn, mx, s, gx, wx, vg, ag, lds in rows:
+        print(f"| `{short_name(name)[:100]}` | {gx} / {wx} | {n} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
+              f"{mx / 1e3:.2f} | {s / tot * 100:.1f}% | {vg}/{ag} | {lds} |")
+
+
+def read_counter(path, counter):
+    """{(role, grid): [values]} of one counter over the dispatches of a counter-collection CSV."""
+    out = collections.defaultdict(list)
+    other = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            role = chain_role(r["Kernel_Name"])
+            key = (role, int(r["Grid_Size"]))
+            (out if role else other)[key if role else (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))].append(
+                float(r["Counter_Value"]))
+    return out, other
+
+
+def main_grid(d, role):
+    cands = {k: v for k, v in d.items() if k[0] == role}
+    if not cands:
+        return None, []
+    k = max(cands, key=lambda k: len(cands[k]))
+    return k[1], cands[k]
+
+
+def cmd_traffic(a):
+    sys.path.insert(0, ROOT)
+    from bench import kernel_source_hash
+
+    res = {"config": a.config, "kernel_source_hash": kernel_source_hash(), "commands": a.command or []}
+    cal = {}
+    for counter, path in (("FETCH_SIZE", a.copy_fetch), ("WRITE_SIZE", a.copy_write)):
+        _, other = read_counter(path, counter)
+        # the copy kernel: the largest per-dispatch value of the copy run
+        vals = [max(v) for v in other.values()]
+        if not vals:
+            raise SystemExit(f"no dispatch with {counter} in {path}")
+        kib = max(vals)
+        cal[counter] = a.copy_bytes / (kib * 1024.0)
+    res["calibration"] = {"copy_bytes": a.copy_bytes, "bytes_per_counted_byte": cal}
+    lines = [f"# HBM traffic per launch, {a.config} configuration\n"]
+    for c in a.command or []:
+        lines.append("    " + c)
+    lines.append("")
+    lines.append(f"Calibration: a device copy of {a.copy_bytes} bytes reads as FETCH_SIZE x "
+                 f"{cal['FETCH_SIZE']:.3f} and WRITE_SIZE x {cal['WRITE_SIZE']:.3f} bytes.\n")
+    lines.append("| launch | grid | dispatches | FETCH bytes | WRITE bytes | HBM bytes per launch |")
+    lines.append("|---|---|---|---|---|---|")
+    fetch, _ = read_counter(a.fetch, "FETCH_SIZE")
+    write, _ = read_counter(a.write, "WRITE_SIZE")
+    for role in ("quantize", "einsum", "gemm"):
+        gf, vf = main_grid(fetch, role)
+        gw, vw = main_grid(write, role)
+        if not vf or not vw:
+            continue
+        fb = sum(vf) / len(vf) * 1024 * cal["FETCH_SIZE"]
+        wb = sum(vw) / len(vw) * 1024 * cal["WRITE_SIZE"]
+        res[role] = {"grid": gf, "dispatches": len(vf), "fetch_bytes": fb, "write_bytes": wb,
+                     "hbm_bytes_per_launch": fb + wb}
+        lines.append(f"| {role} | {gf} | {len(vf)} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} |")
+    path = os.path.join(ROOT, "profiles", f"traffic_{a.config}.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("db")
+    k.add_argument("--title", default="")
+    k.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--config", required=True)
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--command", action="append")
+    a = ap.parse_args()
+    {"kernels": cmd_kernels, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
