@@ -86,6 +86,24 @@ int mxfp8_version(void);
 int mxfp8_device_check(void);
 
 /*
+ * mxfp8_set_splitk_mode -- how the few-token (decode) GEMM kernels combine the
+ * fp32 partial tiles of a K range split across workgroups.  Diagnostic control:
+ * every mode gives the same bits, only the time differs.
+ *
+ *   0  (default) through the L2 cache of one XCD: the splits of a tile are
+ *      consecutive workgroups, which round-robin dispatch places on one XCD.
+ *      The arrival counter records each split's XCD; if any split ran on another
+ *      XCD, the last split to arrive computes the other splits again itself.
+ *   1  through memory (write-through stores, read back past the caches).
+ *   2  as 0, but the last split always recomputes the others (exercises the
+ *      fallback of mode 0).
+ *
+ * Applies to launches made after the call, process-wide.  Returns MXFP8_OK, or
+ * MXFP8_ERR_UNSUPPORTED for another value (the mode is then unchanged).
+ */
+int mxfp8_set_splitk_mode(int mode);
+
+/*
  * mxfp8_quantize -- dynamic MXFP8 quantization of BF16 rows
  * (the standalone quantize launch that vLLM PR #57977, section Purpose, counts
  * per decode step, and that PR #60118, Claims, removes from the o_proj chain).

@@ -39,6 +39,7 @@ SIGNATURES = {
     "mxfp8_status_string": (ctypes.c_char_p, [c_int]),
     "mxfp8_version": (c_int, []),
     "mxfp8_device_check": (c_int, []),
+    "mxfp8_set_splitk_mode": (c_int, [c_int]),
     "mxfp8_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "grouped_fp8_einsum": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
                                    c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
@@ -131,6 +132,14 @@ def _ws_args(need: int, device, stream_ptr: int, workspace: torch.Tensor | None)
 
 def device_check() -> None:
     _check(_lib.mxfp8_device_check(), "mxfp8_device_check")
+
+
+SPLITK_MODES = {"local": 0, "through": 1, "recompute": 2}
+
+
+def set_splitk_mode(mode: str) -> None:
+    """How the decode kernels combine split-K partials ("local", "through", "recompute"); same bits."""
+    _check(_lib.mxfp8_set_splitk_mode(SPLITK_MODES[mode]), "mxfp8_set_splitk_mode")
 
 
 # ----------------------------------------------------------------------------- quantize

@@ -3,7 +3,7 @@
 // Every argument is checked on the host before the first HIP call, so argument
 // errors are reported the same way on a machine without a GPU.  The library
 // allocates nothing, never synchronizes, and keeps no state besides a per-device
-// cache of the architecture check.
+// cache of the architecture check and the split-K combine mode.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -36,6 +36,7 @@ bool overlaps(const Range& a, const Range& b) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 std::atomic<int> g_arch_cache[256];  // 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_splitk_mode{mx::SPLITK_LOCAL};   // see mxfp8_set_splitk_mode
 
 int device_check() {
   int dev = -1;
@@ -116,6 +117,12 @@ MX_API int mxfp8_version(void) { return 100; }
 
 MX_API int mxfp8_device_check(void) { return device_check(); }
 
+MX_API int mxfp8_set_splitk_mode(int mode) {
+  if (mode < mx::SPLITK_LOCAL || mode > mx::SPLITK_RECOMPUTE) return MXFP8_ERR_UNSUPPORTED;
+  g_splitk_mode.store(mode, std::memory_order_relaxed);
+  return MXFP8_OK;
+}
+
 MX_API int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, void* q, int64_t ld_q,
                           int32_t* sf, int64_t ld_sf, void* stream) {
   if (M < 0 || K <= 0 || K % 128) return MXFP8_ERR_SHAPE;
@@ -166,6 +173,7 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
   if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2]))
     return MXFP8_ERR_ALIAS;
   mx::GemmArgs p{};
+  p.splitk_mode = g_splitk_mode.load(std::memory_order_relaxed);
   Range rw;
   if (int s = bind_workspace(mx::plan_gemm(M, G, N, K), workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
   for (const Range& o : outs)
@@ -204,6 +212,7 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
   for (const Range& in : ins)
     if (overlaps(out, in)) return MXFP8_ERR_ALIAS;
   mx::GemmArgs p{};
+  p.splitk_mode = g_splitk_mode.load(std::memory_order_relaxed);
   Range rw;
   if (int s = bind_workspace(mx::plan_gemm(M, 1, N, K), workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
   if (overlaps(rw, out)) return MXFP8_ERR_ALIAS;

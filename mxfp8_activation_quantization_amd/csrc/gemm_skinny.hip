@@ -34,6 +34,8 @@ namespace {
 
 constexpr uint32_t kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked
 constexpr int kUncached = 0x11;              // sc0 | sc1: bypass L1 and L2 (partials cross XCDs)
+constexpr int kL2 = 0x01;                    // sc0: through L1 to the XCD's L2 (partials stay on one XCD)
+constexpr int kLocalMaxSplits = 16;          // per-XCD arrival counts are 4-bit fields
 constexpr int kTileRows = 64;                // weight rows per work item
 constexpr int kChunkTokens = 64;             // tokens per work item (two token tiles)
 constexpr int kStepBytes = 64 * 128;         // one 128-deep step of a 64-row operand tile
@@ -383,10 +385,6 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   const bool computes = tt < MT;
 
   const int ksteps = (int)(p.K / 128);
-  const int k_lo = (int)((int64_t)s * ksteps / S);
-  const int k_hi = (int)((int64_t)(s + 1) * ksteps / S);
-  const int nsteps = k_hi - k_lo;                 // <= kMaxSteps (the plan guarantees it)
-  const int nst = (nsteps + kStageSteps - 1) / kStageSteps;
   const int64_t n_row0 = (int64_t)g * p.N + (int64_t)nt * kTileRows;
   const int64_t m_first = (int64_t)chunk * kChunkTokens;
   const int64_t m_rows = p.M - m_first < kChunkTokens ? p.M - m_first : kChunkTokens;
@@ -403,67 +401,153 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   const Rsrc rxs = make_rsrc_sgpr(p.x_sf + m_first * p.ld_xsf, m_rows * ldxs);
 
   // per-lane offsets: instruction j of this wave covers rows 8n .. 8n+7, n = 4j + wave
-  int vw[2], vx[2], vts[2], vtx[2];
+  int vw[2], vx[2], vts0[2], vtx0[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = 4 * j + wave, r = 8 * n + (lane >> 3), c = (lane & 7) ^ g8(r), ct = (lane & 7) ^ (r & 7);
     vw[j] = r * ldw + c * 16;
     vx[j] = r * ldx + c * 16;
-    // scale table chunk ct = steps 4ct .. 4ct+3 of the range; the whole offset is in the
-    // per-lane register so that the range check sees it (no read past a buffer's end)
-    vts[j] = (r * ksteps + k_lo) * 4 + ct * 16;
-    vtx[j] = r * ldxs + xsfcol0 + k_lo * 4 + ct * 16;
+    // scale table chunk ct = steps 4ct .. 4ct+3 of the range (plus 4 k_lo bytes below);
+    // the whole offset is in the per-lane register so that the range check sees it
+    // (no read past a buffer's end)
+    vts0[j] = r * ksteps * 4 + ct * 16;
+    vtx0[j] = r * ldxs + xsfcol0 + ct * 16;
   }
 
-  // scale tables first (they complete before any stage: loads finish in issue order)
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = 4 * j + wave;
-    dl_load16(rws, wtab + n * 256, vts[j], 0);
-    dl_load16(rxs, xtab + n * 256, vtx[j], 0);
-  }
+  // The K range of split s_ through the pipeline, into a fresh accumulator.  All
+  // threads take part (loads and barriers); waves that own no token tile return zeros.
+  auto run_split = [&](int s_) -> v16f {
+    const int k_lo = (int)((int64_t)s_ * ksteps / S);
+    const int k_hi = (int)((int64_t)(s_ + 1) * ksteps / S);
+    const int nsteps = k_hi - k_lo;               // <= kMaxSteps (the plan guarantees it)
+    const int nst = (nsteps + kStageSteps - 1) / kStageSteps;
+    __syncthreads();                              // LDS of a previous run is no longer read
 
-  // A stage's second step past the range (odd step count) loads the last step
-  // again -- valid addresses -- and is not multiplied.
-  auto issue = [&](int t) {
-    RingStage& st = ring[t % kRing];
+    // scale tables first (they complete before any stage: loads finish in issue order)
 #pragma unroll
-    for (int h = 0; h < kStageSteps; ++h) {
-      const int kk = k_lo + kStageSteps * t + h, k = kk < k_hi ? kk : k_hi - 1;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = 4 * j + wave;
-        dl_load16(rw, st.w[h] + n * 1024, vw[j], k * 128);
-        dl_load16(rx, st.x[h] + n * 1024, vx[j], xcol0 + k * 128);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int n = 4 * j + wave;
+      dl_load16(rws, wtab + n * 256, vts0[j] + k_lo * 4, 0);
+      dl_load16(rxs, xtab + n * 256, vtx0[j] + k_lo * 4, 0);
     }
-  };
 
-  v16f acc = zero16();
-  const int pre = nst < kRing - 1 ? nst : kRing - 1;
-  for (int t = 0; t < pre; ++t) issue(t);
-  for (int t = 0; t < nst; ++t) {
-    // stage t's loads are done when at most the later issued stages remain in flight
-    const int later = (nst - 1 - t) < (kRing - 2) ? (nst - 1 - t) : (kRing - 2);
-    wait_stages<L>(later);
-    asm volatile("s_barrier" ::: "memory");       // every wave's loads of stage t landed; stage t-1 is free
-    if (t + kRing - 1 < nst) issue(t + kRing - 1);
-    if (computes) {
-      const RingStage& st = ring[t % kRing];
+    // A stage's second step past the range (odd step count) loads the last step
+    // again -- valid addresses -- and is not multiplied.
+    auto issue = [&](int t) {
+      RingStage& st = ring[t % kRing];
 #pragma unroll
       for (int h = 0; h < kStageSteps; ++h) {
-        const int j = kStageSteps * t + h;
-        if (j < nsteps) {
-          const int sw = (int)(table_word(wtab, rt * 32 + i, j) >> (8 * q));
-          const int sx = (int)(table_word(xtab, tt * 32 + i, j) >> (8 * q));
-          acc = mfma_scaled<0>(ring_frag(st.w[h], rt, 0, lane), ring_frag(st.x[h], tt, 0, lane), acc, sw, sx);
-          acc = mfma_scaled<2>(ring_frag(st.w[h], rt, 1, lane), ring_frag(st.x[h], tt, 1, lane), acc, sw, sx);
+        const int kk = k_lo + kStageSteps * t + h, k = kk < k_hi ? kk : k_hi - 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = 4 * j + wave;
+          dl_load16(rw, st.w[h] + n * 1024, vw[j], k * 128);
+          dl_load16(rx, st.x[h] + n * 1024, vx[j], xcol0 + k * 128);
+        }
+      }
+    };
+
+    v16f acc = zero16();
+    const int pre = nst < kRing - 1 ? nst : kRing - 1;
+    for (int t = 0; t < pre; ++t) issue(t);
+    for (int t = 0; t < nst; ++t) {
+      // stage t's loads are done when at most the later issued stages remain in flight
+      const int later = (nst - 1 - t) < (kRing - 2) ? (nst - 1 - t) : (kRing - 2);
+      wait_stages<L>(later);
+      asm volatile("s_barrier" ::: "memory");       // every wave's loads of stage t landed; stage t-1 is free
+      if (t + kRing - 1 < nst) issue(t + kRing - 1);
+      if (computes) {
+        const RingStage& st = ring[t % kRing];
+#pragma unroll
+        for (int h = 0; h < kStageSteps; ++h) {
+          const int j = kStageSteps * t + h;
+          if (j < nsteps) {
+            const int sw = (int)(table_word(wtab, rt * 32 + i, j) >> (8 * q));
+            const int sx = (int)(table_word(xtab, tt * 32 + i, j) >> (8 * q));
+            acc = mfma_scaled<0>(ring_frag(st.w[h], rt, 0, lane), ring_frag(st.x[h], tt, 0, lane), acc, sw, sx);
+            acc = mfma_scaled<2>(ring_frag(st.w[h], rt, 1, lane), ring_frag(st.x[h], tt, 1, lane), acc, sw, sx);
+          }
         }
       }
     }
+    return acc;
+  };
+
+  const v16f acc = run_split(s);
+  const int64_t nb = n_row0 + rt * 32, m = m_first + tt * 32 + i;
+  if (S == 1) {
+    if (computes) store_tile<OUT>(p, acc, m, m < p.M, nb, q);
+    return;
   }
-  finish_tile<MT, OUT>(p, acc, tc, s, S, rt, tt, lane, tid, n_row0 + rt * 32, m_first + tt * 32 + i, computes,
-                       &s_last);
+  if (p.splitk_mode == SPLITK_THROUGH || S > kLocalMaxSplits) {
+    finish_tile<MT, OUT>(p, acc, tc, s, S, rt, tt, lane, tid, nb, m, computes, &s_last);
+    return;
+  }
+
+  // Split K through the XCD's L2.  The S items of a tile are consecutive work
+  // items, which the XCD-aware numbering places on one XCD when workgroups are
+  // dealt to the XCDs in turn; their L2 is then shared, and a partial tile needs
+  // to reach L2 only, not memory (measured: the write acknowledgement then takes
+  // about a third as long).  The arrival counter is 64 bits, updated by coherent
+  // system-scope atomics: the low word counts arrivals, the high word holds a
+  // 4-bit count per XCD.  The last arriver adds the partials in split order when
+  // every other split ran on its own XCD; otherwise -- workgroups dealt some
+  // other way -- a partial may sit in another XCD's L2, and the last arriver
+  // computes those splits again itself.  Either way the sum is the same.
+  constexpr int TILE_FLOATS = 2 * MT * 16 * 64;
+  constexpr int TILE_BYTES = TILE_FLOATS * 4;
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_partials + (int64_t)tc * S * TILE_FLOATS, 0, S * TILE_BYTES, kRsrcFlags);
+  const int my_off = ((rt * MT + tt) * 64 + lane) * 64;     // bytes within a split's tile
+  if (computes) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const v4i v = {__float_as_int(acc[4 * k]), __float_as_int(acc[4 * k + 1]), __float_as_int(acc[4 * k + 2]),
+                     __float_as_int(acc[4 * k + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rp, s * TILE_BYTES + my_off + 16 * k, 0, kL2);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  unsigned long long* cnt = reinterpret_cast<unsigned long long*>(p.ws_counters) + tc;
+  if (tid == 0) {
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    xcc &= 7;
+    const unsigned long long old =
+        __hip_atomic_fetch_add(cnt, 1ull | (1ull << (32 + 4 * xcc)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const bool last = (unsigned)old == (unsigned)(S - 1);
+    const bool here = ((old >> (32 + 4 * xcc)) & 15ull) == (unsigned long long)(S - 1) &&
+                      p.splitk_mode != SPLITK_RECOMPUTE;
+    s_last = (last ? 1 : 0) | (here ? 2 : 0);
+  }
+  __syncthreads();
+  const int fl = s_last;
+  if (!(fl & 1)) return;
+  v16f tot = zero16();
+  for (int s2 = 0; s2 < S; ++s2) {
+    v16f part = acc;
+    if (s2 != s) {
+      if (fl & 2) {
+        if (computes) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rp, s2 * TILE_BYTES + my_off + 16 * k, 0, kL2);
+            part[4 * k] = __int_as_float(v.x);
+            part[4 * k + 1] = __int_as_float(v.y);
+            part[4 * k + 2] = __int_as_float(v.z);
+            part[4 * k + 3] = __int_as_float(v.w);
+          }
+        }
+      } else {
+        part = run_split(s2);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tot[e] += part[e];
+  }
+  if (computes) store_tile<OUT>(p, tot, m, m < p.M, nb, q);
+  if (tid == 0) __hip_atomic_store(cnt, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 template <int MT, int OUT>

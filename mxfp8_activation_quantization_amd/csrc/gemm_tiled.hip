@@ -639,7 +639,7 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K) {
   const int mt = M <= 32 ? 1 : 2;
   const int64_t chunks = (M + 63) / 64;
   const int64_t tiles = G * (N / 64) * chunks;
-  pl.skinny = M <= kSkinnyMaxTokens && tiles * 4 <= kCounterBytes;
+  pl.skinny = M <= kSkinnyMaxTokens && tiles * 8 <= kCounterBytes;     // one 64-bit counter per tile
   if (!pl.skinny) {
     const int64_t bn = N % 256 == 0 ? 256 : 128;
     pl.workgroups = G * (N / bn) * ((M + 255) / 256);     // E4M3 activations (BF16: twice as many)

@@ -9,6 +9,12 @@ namespace mx {
 // One GEMM launch: G groups of D[m, g*N + n] = sum_k X[m, g*K + k] * W[g][n][k].
 // Strides are in elements of each array (bytes for codes and scale bytes, 2-byte
 // units for BF16, int32 words for packed input scales).
+// How the decode kernels combine split-K partial tiles (all give the same bits):
+// through the L2 of one XCD when every split of a tile ran there (checked at run
+// time, with recomputation of the other splits as the fallback), always through
+// memory, or -- to test the fallback -- always by recomputation.
+enum SplitKMode { SPLITK_LOCAL = 0, SPLITK_THROUGH = 1, SPLITK_RECOMPUTE = 2 };
+
 struct GemmArgs {
   const void* x;          // activations: BF16 or E4M3 codes, rows m, ld_x elements apart
   int64_t ld_x;
@@ -25,6 +31,7 @@ struct GemmArgs {
   int64_t ld_zb;
   uint32_t* ws_counters;  // split-K arrival counters (zero between calls), or null
   float* ws_partials;     // split-K fp32 partial tiles, or null
+  int splitk_mode;        // how split-K partials are combined (SplitKMode)
 };
 
 // Kernel choice and scratch needs of one GEMM launch: a pure function of

@@ -173,6 +173,13 @@ def test_workspace_errors():
     assert gemm(K=512, ws=None, ws_bytes=0) != B.MXFP8_ERR_WORKSPACE      # one K slice: none needed
 
 
+def test_splitk_mode_control():
+    assert LIB.mxfp8_set_splitk_mode(3) == B.MXFP8_ERR_UNSUPPORTED
+    assert LIB.mxfp8_set_splitk_mode(-1) == B.MXFP8_ERR_UNSUPPORTED
+    for m in (1, 2, 0):
+        assert LIB.mxfp8_set_splitk_mode(m) == B.MXFP8_OK
+
+
 def test_binding_raises_value_error_on_argument_status():
     with pytest.raises(ValueError):
         B._check(B.MXFP8_ERR_SHAPE, "test")

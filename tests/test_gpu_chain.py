@@ -145,8 +145,49 @@ def test_split_k_workspace_counters_return_to_zero(lib):
     torch.cuda.synchronize()
     assert all(torch.equal(o, outs[0]) for o in outs)
     tiles = (N // 64) * 1
-    assert int(ws[:4 * tiles].view(torch.int32).abs().sum()) == 0
+    assert int(ws[:8 * tiles].view(torch.int32).abs().sum()) == 0      # one 64-bit counter per tile
     assert np.array_equal(to_np(outs[0]), mx.bf16_round(cr.gemm_nt(aq, asf, bq, bsf)))
+
+
+@pytest.mark.parametrize("kind,M,G,N,K", [("gemm", 48, 1, 256, 4096), ("gemm", 64, 1, 5120, 8192),
+                                          ("gemm", 5, 1, 128, 2176), ("einsum", 64, 8, 1024, 4096),
+                                          ("einsum", 33, 3, 256, 1024)])
+def test_split_k_combine_modes_give_identical_bits(lib, kind, M, G, N, K):
+    """The decode kernels combine split-K partials through one XCD's L2 (default), through memory, or by
+    recomputing the other splits (the fallback when a tile's splits ran on different XCDs): all three give
+    the same bits, equal to the oracle in the exact regime, and leave the counters at zero."""
+    from mxfp8_activation_quantization_amd import binding as B
+    rng = np.random.default_rng(300 + M + N)
+    aq, asf = exact_operands(rng, M, G * K)
+    wq, wsf = exact_operands(rng, G * N, K)
+    a_t, asf_t = u8_to_dev(aq), i32_to_dev(asf)
+    if kind == "gemm":
+        w_t, wsf_t = u8_to_dev(wq), i32_to_dev(wsf)
+    else:
+        w_t, wsf_t = u8_to_dev(wq.reshape(G, N, K)), i32_to_dev(wsf.reshape(G, N, K // 128))
+    need = (B.lib().fp8_gemm_nt_workspace_size(M, N, K) if kind == "gemm"
+            else B.lib().grouped_fp8_einsum_workspace_size(M, G, K, N))
+    assert need > 0                                                       # the shape is split along K
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    outs = {}
+    try:
+        for mode in ("local", "through", "recompute", "local"):
+            lib.set_splitk_mode(mode)
+            if kind == "gemm":
+                outs[mode] = to_np(lib.fp8_gemm_nt(a_t, asf_t, w_t, wsf_t, workspace=ws))
+            else:
+                outs[mode] = to_np(lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="bf16", workspace=ws))
+            torch.cuda.synchronize()
+            assert int(ws[:4096].view(torch.int32).abs().sum()) == 0, mode
+    finally:
+        lib.set_splitk_mode("local")
+    assert np.array_equal(outs["through"], outs["local"])
+    assert np.array_equal(outs["recompute"], outs["local"])
+    if kind == "gemm":
+        ref = mx.bf16_round(cr.gemm_nt(aq, asf, wq, wsf))
+    else:
+        ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
+    assert np.array_equal(outs["local"], ref)
 
 
 # --------------------------------------------------------------------------- configs
