@@ -122,7 +122,8 @@ def copy_calibration(torch, mib):
 
 
 def time_arm_graphs(torch, graphs, stream, steps, warmup):
-    """Average µs per replay of a list of captured graphs, replayed round-robin on `stream`."""
+    """Average µs per replay of a list of captured graphs, replayed round-robin on `stream`
+    (HIP events on that stream)."""
     with torch.cuda.stream(stream):
         for i in range(warmup):
             graphs[i % len(graphs)].replay()
@@ -152,19 +153,20 @@ def sweep(torch, L, Ms, dims, w, stream, args):
                  "wb_q": w["wb_q"].clone(), "wb_sf": w["wb_sf"].clone()} for r in range(R)]
         res = {"M": M}
         for arm in ("chain", "x_fused"):
-            graphs = []
-            for s in sets:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.stream(stream):
+            # one graph with the chain once per rotating set, in a row (as consecutive layers)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                for s in sets:
                     L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm, stream=stream)
-                    stream.synchronize()
-                    with torch.cuda.graph(g, stream=stream):
+                stream.synchronize()
+                with torch.cuda.graph(g, stream=stream):
+                    for s in sets:
                         L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm,
                                        stream=stream)
-                graphs.append(g)
             steps = max(5, min(args.steps, int(2e5 // max(1, M))))
-            res[f"{arm}_us"] = time_arm_graphs(torch, graphs, stream, steps, min(args.warmup, steps))
-            del graphs
+            reps = max(1, -(-steps // R))
+            res[f"{arm}_us"] = time_arm_graphs(torch, [g], stream, reps, max(1, reps // 4)) / R
+            del g
         flop = sum(chain_flops(M, G, K, N, P).values())
         nb = chain_bytes(M, G, K, N, P)
         us = res["chain_us"]
@@ -264,47 +266,50 @@ def main():
             L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm, stream=stream)
 
     def capture(arm):
-        graphs = []
-        for s in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(stream):
-                launch_arm(arm, s)                      # warm: allocations of intermediate buffers
-                stream.synchronize()
-                with torch.cuda.graph(g, stream=stream):
-                    launch_arm(arm, s)
-            graphs.append(g)
-        torch.cuda.synchronize()
-        return graphs
-
-    def time_graphs(graphs, steps, warmup):
+        """One graph holding the chain once per rotating set, in a row (as consecutive layers)."""
+        g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
-            for i in range(warmup):
-                graphs[i % R].replay()
+            for s in sets:
+                launch_arm(arm, s)                      # warm: allocations of intermediate buffers
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for s in sets:
+                    launch_arm(arm, s)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graphs(g, steps, warmup):
+        """µs per chain call: replays of the R-chain graph covering at least `steps` calls."""
+        n_rep, n_warm = max(1, -(-steps // R)), max(1, -(-warmup // R))
+        with torch.cuda.stream(stream):
+            for _ in range(n_warm):
+                g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         with torch.cuda.stream(stream):
             e0.record(stream)
-            for i in range(steps):
-                graphs[i % R].replay()
+            for _ in range(n_rep):
+                g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+        return e0.elapsed_time(e1) / (n_rep * R), wall / (n_rep * R) * 1e3
 
     arms = [a for a in args.arms.split(",") if a]
     results = {}
     for arm in arms:
-        graphs = capture(arm)
-        ms_ev, ms_wall = time_graphs(graphs, args.steps, args.warmup)
+        g = capture(arm)
+        ms_ev, ms_wall = time_graphs(g, args.steps, args.warmup)
         results[arm] = {"us_per_call": ms_ev * 1e3, "wall_us_per_call": ms_wall * 1e3}
         print(f"[bench] arm {arm}: {ms_ev * 1e3:.2f} us/call (graph replay)", file=sys.stderr, flush=True)
-        del graphs
+        del g
 
-    # Per-kernel durations: each launch of the headline chain captured alone in graphs
-    # (one launch per rotating set, so inputs stay cold), replayed back to back and
-    # timed with HIP events on the launch stream -- the kernel's own duration plus
-    # the small gap between graph nodes, comparable with a profiler's kernel trace.
+    # Per-kernel durations: each launch of the headline chain captured alone in one
+    # graph, at least 16 times in a row over the rotating sets (inputs stay cold), and
+    # the graph replayed and timed with HIP events on the launch stream -- the kernel's
+    # own duration plus the small gap between graph nodes, comparable with a
+    # profiler's kernel trace (one launch per graph would time the host's submission).
     def launch_one(kind, s):
         if kind == "quantize":
             L.mxfp8_quantize(s["x"], q=s["x_q"], sf=s["x_sf"], stream=stream)
@@ -315,19 +320,21 @@ def main():
             L.fp8_gemm_nt(s["z_q"], s["z_sf"], s["wb_q"], s["wb_sf"], d=s["out"], stream=stream)
 
     t_k = {}
+    reps = max(1, -(-16 // R))                     # at least 16 launches per graph
     for kind in ("quantize", "einsum", "gemm"):
-        graphs = []
-        for s in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(stream):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for s in sets:
                 launch_one(kind, s)
-                stream.synchronize()
-                with torch.cuda.graph(g, stream=stream):
-                    launch_one(kind, s)
-            graphs.append(g)
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(reps):
+                    for s in sets:
+                        launch_one(kind, s)
         torch.cuda.synchronize()
-        t_k[kind] = time_arm_graphs(torch, graphs, stream, args.steps, args.warmup)
-        del graphs
+        t_k[kind] = time_arm_graphs(torch, [g], stream, max(1, args.steps // (reps * R)) + 1,
+                                    max(1, args.warmup // (reps * R))) / (reps * R)
+        del g
 
     flops = chain_flops(M, G, K, N, P)
     nbytes = chain_bytes(M, G, K, N, P)

@@ -202,6 +202,20 @@ __device__ __forceinline__ void dl_load4(const Rsrc& r, const void* lds, int vof
                :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
 }
 
+// 16 bytes per lane from memory into registers.  Inline assembly like the LDS-DMA
+// loads above, for the same reason: the caller counts its loads (s_waitcnt
+// vmcnt) and ties the result registers to its own wait (`tie_after_wait`); the
+// compiler's own counting would not see the LDS-DMA loads in flight.
+__device__ __forceinline__ v4i buf_load16(const Rsrc& r, int voff, int soff) {
+  v4i v;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(v) : "v"(voff), "s"(r.v), "s"(soff) : "memory");
+  return v;
+}
+
+// Declares a register written by an asm load valid from here on (place it after
+// the s_waitcnt that covers the load): the compiler may not move a use above it.
+__device__ __forceinline__ void tie_after_wait(v4i& v) { asm volatile("" : "+v"(v)); }
+
 // LDS reads with a constant offset (inline assembly: see the direct-to-LDS GEMM).
 // The result is not valid until a later s_waitcnt lgkmcnt(0) that the caller
 // ties to the result registers.

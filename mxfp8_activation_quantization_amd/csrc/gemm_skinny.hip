@@ -360,7 +360,7 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-template <int MT, int OUT>
+template <int MT, int OUT, bool XB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   static_assert(kRing == 4, "wait_stages covers up to kRing - 2 stages in flight");
@@ -397,8 +397,16 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   // past M arrive as zeros and nothing past row M is read.  The scale tables may
   // read up to 31 words past a row's K range: the next row's words (unused), or
   // zeros past the end of the buffer.
-  const Rsrc rx = make_rsrc_sgpr(static_cast<const uint8_t*>(p.x) + m_first * ldx, m_rows * ldx);
-  const Rsrc rxs = make_rsrc_sgpr(p.x_sf + m_first * p.ld_xsf, m_rows * ldxs);
+  const Rsrc rx = make_rsrc_sgpr(static_cast<const uint8_t*>(p.x) + m_first * ldx * (XB ? 2 : 1),
+                                 m_rows * ldx * (XB ? 2 : 1));
+  const Rsrc rxs = make_rsrc_sgpr(XB ? nullptr : p.x_sf + m_first * p.ld_xsf, XB ? 0 : m_rows * ldxs);
+  const Rsrc rnull = make_rsrc_sgpr(p.w, 0);       // zero bytes: every lane out of range, nothing read
+
+  // BF16 activations (quantized here): thread -> token row xr, 32-element block xb of
+  // each step; its 64 bytes per step are four 16-byte loads at vxb + 16 u (row part in
+  // the per-lane register, so rows past M read as zeros), step k at scalar offset 256 k.
+  const int xr = tid >> 2, xb = tid & 3, gxr = g8(xr);
+  const int vxb = xr * ldx * 2 + xcol0 * 2 + xb * 64;
 
   // per-lane offsets: instruction j of this wave covers rows 8n .. 8n+7, n = 4j + wave
   int vw[2], vx[2], vts0[2], vtx0[2];
@@ -428,7 +436,114 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
     for (int j = 0; j < 2; ++j) {
       const int n = 4 * j + wave;
       dl_load16(rws, wtab + n * 256, vts0[j] + k_lo * 4, 0);
-      dl_load16(rxs, xtab + n * 256, vtx0[j] + k_lo * 4, 0);
+      if constexpr (!XB) dl_load16(rxs, xtab + n * 256, vtx0[j] + k_lo * 4, 0);
+    }
+
+    // multiplies stage t (all threads call it; waves without a token tile skip)
+    auto mma_stage = [&](int t, v16f& acc) {
+      if (computes) {
+        const RingStage& st = ring[t % kRing];
+#pragma unroll
+        for (int h = 0; h < kStageSteps; ++h) {
+          const int j = kStageSteps * t + h;
+          if (j < nsteps) {
+            const int sw = (int)(table_word(wtab, rt * 32 + i, j) >> (8 * q));
+            const int sx = (int)(table_word(xtab, tt * 32 + i, j) >> (8 * q));
+            acc = mfma_scaled<0>(ring_frag(st.w[h], rt, 0, lane), ring_frag(st.x[h], tt, 0, lane), acc, sw, sx);
+            acc = mfma_scaled<2>(ring_frag(st.w[h], rt, 1, lane), ring_frag(st.x[h], tt, 1, lane), acc, sw, sx);
+          }
+        }
+      }
+    };
+
+    if constexpr (XB) {
+      // BF16 activations.  Weights stream into the ring as with E4M3 activations;
+      // each thread loads its token's 32-element block of the two steps of a stage
+      // into registers two stages ahead, then quantizes it (its own amax: the
+      // quantizer's rule) into the stage's activation slot and the scale table.  Two
+      // register sets alternate, so the loop is unrolled by two.  Every step issues
+      // the same loads -- switched off (zero-byte resource) past the last stage --
+      // so the wait counts are constants: a step needs the activation registers of
+      // stage t+2, after which only the previous step's batch (4 weight + 8
+      // activation loads) may still be in flight.
+      struct XRegs { v4i v[8]; };
+      auto load_x = [&](XRegs& X, int t) {
+#pragma unroll
+        for (int h = 0; h < kStageSteps; ++h) {
+          const int k = k_lo + kStageSteps * t + h;
+          const bool on = t < nst && k < k_hi;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) X.v[4 * h + u] = buf_load16(on ? rx : rnull, vxb + 16 * u, k * 256);
+        }
+      };
+      auto issue_w = [&](int t) {
+        RingStage& st = ring[t % kRing];
+        const bool on = t < nst;
+#pragma unroll
+        for (int h = 0; h < kStageSteps; ++h) {
+          const int kk = k_lo + kStageSteps * t + h, k = kk < k_hi ? kk : k_hi - 1;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dl_load16(on ? rw : rnull, st.w[h] + (4 * j + wave) * 1024, vw[j], k * 128);
+        }
+      };
+      auto quantize_x = [&](XRegs& X, int t) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tie_after_wait(X.v[u]);
+        RingStage& st = ring[t % kRing];
+        uint8_t* xt = reinterpret_cast<uint8_t*>(xtab);
+#pragma unroll
+        for (int h = 0; h < kStageSteps; ++h) {
+          uint32_t w[16];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            w[4 * u] = (uint32_t)X.v[4 * h + u].x;
+            w[4 * u + 1] = (uint32_t)X.v[4 * h + u].y;
+            w[4 * u + 2] = (uint32_t)X.v[4 * h + u].z;
+            w[4 * u + 3] = (uint32_t)X.v[4 * h + u].w;
+          }
+          uint32_t am = 0;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) am = amax_pair(am, w[k]);
+          const int e = scale_exp_from_amax(fold_pair(am));
+          const float sc = exp2_int(e);
+          uint32_t c[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) c[k] = encode4(w[2 * k], w[2 * k + 1], sc);
+          *reinterpret_cast<uint4*>(st.x[h] + 16 * (8 * xr + ((2 * xb) ^ gxr))) = make_uint4(c[0], c[1], c[2], c[3]);
+          *reinterpret_cast<uint4*>(st.x[h] + 16 * (8 * xr + ((2 * xb + 1) ^ gxr))) = make_uint4(c[4], c[5], c[6], c[7]);
+          const int j = kStageSteps * t + h;
+          xt[4 * (xr * 32 + (((j >> 2) ^ (xr & 7)) << 2) + (j & 3)) + xb] = (uint8_t)(e + 127);
+        }
+      };
+
+      v16f acc = zero16();
+      XRegs A, B;
+      load_x(A, 0);
+      load_x(B, 1);
+      issue_w(0);
+      issue_w(1);
+      issue_w(2);
+      wait_vmcnt<0>();
+      quantize_x(A, 0);
+      quantize_x(B, 1);
+      load_x(A, 2);
+      load_x(B, 3);
+      // step t: stage t+2's registers are set (t & 1); loads after them: one batch
+      auto step = [&](XRegs& X, int t, bool first) {
+        if (first) wait_vmcnt<8>();
+        else wait_vmcnt<12>();
+        asm volatile("s_barrier" ::: "memory");     // stage t landed everywhere; stages t-1, t-2 are free
+        if (t + 2 < nst) quantize_x(X, t + 2);
+        issue_w(t + 3);
+        load_x(X, t + 4);
+        mma_stage(t, acc);
+      };
+      for (int t = 0; t < nst; t += 2) {
+        step(A, t, t == 0);
+        if (t + 1 < nst) step(B, t + 1, false);
+      }
+      wait_vmcnt<0>();                               // the switched-off loads of the last steps
+      return acc;
     }
 
     // A stage's second step past the range (odd step count) loads the last step
@@ -456,19 +571,7 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
       wait_stages<L>(later);
       asm volatile("s_barrier" ::: "memory");       // every wave's loads of stage t landed; stage t-1 is free
       if (t + kRing - 1 < nst) issue(t + kRing - 1);
-      if (computes) {
-        const RingStage& st = ring[t % kRing];
-#pragma unroll
-        for (int h = 0; h < kStageSteps; ++h) {
-          const int j = kStageSteps * t + h;
-          if (j < nsteps) {
-            const int sw = (int)(table_word(wtab, rt * 32 + i, j) >> (8 * q));
-            const int sx = (int)(table_word(xtab, tt * 32 + i, j) >> (8 * q));
-            acc = mfma_scaled<0>(ring_frag(st.w[h], rt, 0, lane), ring_frag(st.x[h], tt, 0, lane), acc, sw, sx);
-            acc = mfma_scaled<2>(ring_frag(st.w[h], rt, 1, lane), ring_frag(st.x[h], tt, 1, lane), acc, sw, sx);
-          }
-        }
-      }
+      mma_stage(t, acc);
     }
     return acc;
   };
@@ -550,9 +653,9 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   if (tid == 0) __hip_atomic_store(cnt, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-template <int MT, int OUT>
+template <int MT, int OUT, bool XB>
 static hipError_t launch_stream(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  hipLaunchKernelGGL((stream_kernel<MT, OUT>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p, (int)G,
+  hipLaunchKernelGGL((stream_kernel<MT, OUT, XB>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p, (int)G,
                      plan.n_tiles, plan.chunks, plan.splits);
   return hipGetLastError();
 }
@@ -568,13 +671,13 @@ template <int MT>
 static hipError_t dispatch(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,
                            hipStream_t s) {
   if (x_bf16) {
-    if (out == OUT_BF16) return launch_mt<MT, true, OUT_BF16>(p, plan, G, s);
-    if (out == OUT_MX) return launch_mt<MT, true, OUT_MX>(p, plan, G, s);
-    return launch_mt<MT, true, OUT_BOTH>(p, plan, G, s);
+    if (out == OUT_BF16) return launch_stream<MT, OUT_BF16, true>(p, plan, G, s);
+    if (out == OUT_MX) return launch_stream<MT, OUT_MX, true>(p, plan, G, s);
+    return launch_stream<MT, OUT_BOTH, true>(p, plan, G, s);
   }
-  if (out == OUT_BF16) return launch_stream<MT, OUT_BF16>(p, plan, G, s);
-  if (out == OUT_MX) return launch_stream<MT, OUT_MX>(p, plan, G, s);
-  return launch_stream<MT, OUT_BOTH>(p, plan, G, s);
+  if (out == OUT_BF16) return launch_stream<MT, OUT_BF16, false>(p, plan, G, s);
+  if (out == OUT_MX) return launch_stream<MT, OUT_MX, false>(p, plan, G, s);
+  return launch_stream<MT, OUT_BOTH, false>(p, plan, G, s);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,

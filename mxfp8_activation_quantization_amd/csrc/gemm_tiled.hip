@@ -424,7 +424,7 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   // to itself the compiler keeps one address register per stage and tile, runs
   // out of registers and spills -- and a spill reload in this loop would wait for
   // every load in flight).  The compiler does not see these reads complete, so
-  // wait_frags() waits for them and ties the registers to that wait.
+  // wait_early() and wait_late() wait for them and tie the registers to those waits.
   const int gi = dl_g(i);
   const int off_lo = 64 * i + 16 * (q ^ gi), off_hi = 64 * i + 16 * ((2 + q) ^ gi);
   const int base = (int)lds_addr(smem);
@@ -452,23 +452,41 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
       F.fx[c] = join8(lds_read16<D + Lds::X + c * 2048>(xl), lds_read16<D + Lds::X + c * 2048>(xh));
     }
   };
-  auto read = [&](auto stage_tag, Frags& F) {
-    static_for<C::TN + C::TM>([&](auto r_tag) { read_tile(r_tag, stage_tag, F); });
+  // Read order of a stage's tiles: what the first half of the MFMAs needs (weight
+  // tiles 0 .. TN/2-1 and every token tile, in the order those MFMAs use them)
+  // first, the weight tiles of the second half last; a step then waits only for
+  // the first group before it starts, and for the rest before its second half.
+  constexpr auto order = [](int k) constexpr {
+    if (k == 0) return 0;                                   // W0
+    if (k <= C::TM) return C::TN + k - 1;                   // X0 .. X(TM-1)
+    return k - C::TM;                                       // W1 .. W(TN-1)
   };
-  auto wait_frags = [&](Frags& F) {
-    static_assert(C::TN == 4 && C::TM <= 4, "register ties below list four tiles per operand");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(F.fw[0]), "+v"(F.fw[1]), "+v"(F.fw[2]), "+v"(F.fw[3]), "+v"(F.sw[0]), "+v"(F.sw[1]),
-                   "+v"(F.sw[2]), "+v"(F.sw[3]));
+  constexpr int LATE_LDS_OPS = 3 * (C::TN / 2);             // scale word + two halves per late tile
+  auto read = [&](auto stage_tag, Frags& F) {
+    static_for<C::TN + C::TM>([&](auto k_tag) {
+      read_tile(std::integral_constant<int, order(decltype(k_tag)::value)>{}, stage_tag, F);
+    });
+  };
+  // waits for the tiles of the first half (all but the last LATE_LDS_OPS LDS reads),
+  // then for the rest; each ties the registers it covers to its wait
+  auto wait_early = [&](Frags& F) {
+    static_assert(C::TN == 4 && C::TM <= 4, "register ties below list the tiles by name");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(F.fw[0]), "+v"(F.fw[1]) : "n"(LATE_LDS_OPS));
+    asm volatile("" : "+v"(F.sw[0]), "+v"(F.sw[1]));
     if constexpr (C::TM == 4)
       asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.fx[2]), "+v"(F.fx[3]), "+v"(F.sx[0]), "+v"(F.sx[1]),
                    "+v"(F.sx[2]), "+v"(F.sx[3]));
     else
       asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.sx[0]), "+v"(F.sx[1]));
 #pragma unroll
-    for (int a = 0; a < C::TN; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
+    for (int a = 0; a < C::TN / 2; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
 #pragma unroll
     for (int c = 0; c < C::TM; ++c) F.sx[c] = (int)((uint32_t)F.sx[c] >> (8 * q));
+  };
+  auto wait_late = [&](Frags& F) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F.fw[2]), "+v"(F.fw[3]), "+v"(F.sw[2]), "+v"(F.sw[3]));
+#pragma unroll
+    for (int a = C::TN / 2; a < C::TN; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
   };
   // half H (0, 1) of the TN x TM MFMAs of a stage; KS = stage parity (which 64 bytes of the K-step)
   auto mma = [&](const Frags& F, auto ks_tag, auto half_tag) {
@@ -504,7 +522,7 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   auto step = [&](Frags& cur, Frags& nxt, auto stage_tag, int t) {
     constexpr int J = decltype(stage_tag)::value;     // t % 16
     constexpr int KS = J & 1;
-    wait_frags(cur);
+    wait_early(cur);
     mma(cur, std::integral_constant<int, KS>{}, H0{});
     __builtin_amdgcn_sched_barrier(0);
     // loads issued after stage t+1's: stages t+2 and t+3, plus scale group s+1
@@ -513,6 +531,7 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
     asm volatile("s_barrier" ::: "memory");
     if constexpr (J % 8 == 0) issue_scales(t / 8 + 1, 8 * (t / 8 + 1) < nst);
     const bool refill = t + 4 < nst;
+    wait_late(cur);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NMF>([&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
@@ -523,7 +542,7 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
         constexpr int o = m * PER + decltype(k_tag)::value;   // even: read o/2, odd: load o/2
         if constexpr (o < 2 * L) {
           if constexpr (o % 2 == 0)
-            read_tile(std::integral_constant<int, o / 2>{}, std::integral_constant<int, (J + 1) % 16>{}, nxt);
+            read_tile(std::integral_constant<int, order(o / 2)>{}, std::integral_constant<int, (J + 1) % 16>{}, nxt);
           else
             issue_one(std::integral_constant<int, o / 2>{}, J % 4, t + 4, refill);
         }
