@@ -33,18 +33,22 @@
  *     row strides <= 2^23 bytes (scale rows <= 2^16 bytes); otherwise
  *     MXFP8_ERR_SHAPE.
  *   - Outputs must not overlap inputs or each other (MXFP8_ERR_ALIAS).
- *   - Workspace: the GEMM entry points may need device scratch for split-K
- *     partial sums; the matching *_workspace_size() call gives the bytes for a
- *     shape (0 = none needed, pointer may be NULL).  The caller owns it, zero-
- *     fills it once before first use (256-byte aligned).  Its first 64 KiB hold
- *     split-K arrival counters, which every call leaves at zero when it
- *     completes; the rest is scratch.  Calls of any shape may therefore reuse one
- *     workspace one after another (same stream), but calls that run
- *     concurrently (other streams) must not share one.
+ *   - Workspace: the GEMM entry points may need device scratch -- split-K
+ *     partial sums, and, for BF16 activations with more than 256 rows, the
+ *     activations quantized to MXFP8 (the many-token kernel reads E4M3; the
+ *     library quantizes BF16 input with mxfp8_quantize first).  The matching
+ *     *_workspace_size(kind, shape) call gives the bytes (0 = none needed,
+ *     pointer may be NULL).  The caller owns it, zero-fills it once before first
+ *     use (256-byte aligned).  Split-K calls keep arrival counters in its first
+ *     64 KiB and leave them at zero when they complete; the rest is scratch.
+ *     Calls of any shape may therefore reuse one workspace one after another
+ *     (same stream), but calls that run concurrently (other streams) must not
+ *     share one.
  *   - Non-finite inputs are outside the contract (codes then unspecified).
- *   - Results are deterministic: the same inputs give the same bytes, and the
- *     kernel choice depends only on (M, G, N, K), never on the activation kind
- *     or the output mode, so BF16 and pre-quantized x give identical results.
+ *   - Results are deterministic: the same inputs give the same bytes, and BF16
+ *     and pre-quantized activations give identical results (few rows: the
+ *     kernel quantizes BF16 in its load path with the quantizer's rule and the
+ *     same split plan; many rows: the quantizer runs first).
  */
 #ifndef MXFP8_H
 #define MXFP8_H
@@ -137,7 +141,7 @@ int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x,
  *           optional BF16 output [M][ld_zb] (G*N columns).
  * At least one of z_q / z_bf16 must be given (z_q and z_sf together).
  *   workspace, workspace_bytes
- *           split-K scratch, at least grouped_fp8_einsum_workspace_size(M, G, K, N)
+ *           scratch, at least grouped_fp8_einsum_workspace_size(x_kind, M, G, K, N)
  *           bytes (see the conventions above).
  * K and N must be positive multiples of 128 (N % 128 == 0 keeps every scale
  * word of z inside one group: PR #60118, Details, the o_lora_rank % 128 gate).
@@ -149,8 +153,9 @@ int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x
                        void* z_bf16, int64_t ld_zb,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes grouped_fp8_einsum needs for this shape (0 = none); -1 for an invalid shape. */
-int64_t grouped_fp8_einsum_workspace_size(int64_t M, int64_t G, int64_t K, int64_t N);
+/* Workspace bytes grouped_fp8_einsum needs for this activation kind and shape (0 = none);
+ * -1 for an invalid kind or shape. */
+int64_t grouped_fp8_einsum_workspace_size(int x_kind, int64_t M, int64_t G, int64_t K, int64_t N);
 
 /*
  * fp8_gemm_nt -- the wo_b projection, recipe (1,1,32): both operands K-contiguous
@@ -160,7 +165,7 @@ int64_t grouped_fp8_einsum_workspace_size(int64_t M, int64_t G, int64_t K, int64
  *   a_kind, a, ld_a, a_sf, ld_asf   activation rows m in [0, M), K columns (as in the einsum)
  *   b       E4M3 [N][K] bytes, contiguous      b_sf  int32 [N][K/128], contiguous
  *   d       BF16 [M][ld_d], N columns (output)
- *   workspace, workspace_bytes   split-K scratch, at least fp8_gemm_nt_workspace_size(M, N, K) bytes
+ *   workspace, workspace_bytes   scratch, at least fp8_gemm_nt_workspace_size(a_kind, M, N, K) bytes
  * K and N must be positive multiples of 128.
  */
 int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf,
@@ -169,8 +174,9 @@ int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, in
                 void* d, int64_t ld_d,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes fp8_gemm_nt needs for this shape (0 = none); -1 for an invalid shape. */
-int64_t fp8_gemm_nt_workspace_size(int64_t M, int64_t N, int64_t K);
+/* Workspace bytes fp8_gemm_nt needs for this activation kind and shape (0 = none);
+ * -1 for an invalid kind or shape. */
+int64_t fp8_gemm_nt_workspace_size(int a_kind, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

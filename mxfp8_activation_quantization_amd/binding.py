@@ -43,10 +43,10 @@ SIGNATURES = {
     "mxfp8_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "grouped_fp8_einsum": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
                                    c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
-    "grouped_fp8_einsum_workspace_size": (c_i64, [c_i64, c_i64, c_i64, c_i64]),
+    "grouped_fp8_einsum_workspace_size": (c_i64, [c_int, c_i64, c_i64, c_i64, c_i64]),
     "fp8_gemm_nt": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64,
                             c_vp, c_i64, c_vp]),
-    "fp8_gemm_nt_workspace_size": (c_i64, [c_i64, c_i64, c_i64]),
+    "fp8_gemm_nt_workspace_size": (c_i64, [c_int, c_i64, c_i64, c_i64]),
 }
 
 
@@ -218,7 +218,7 @@ def grouped_fp8_einsum(x: torch.Tensor, x_sf: torch.Tensor | None, w: torch.Tens
     else:
         z_bf16 = None
     sp = _stream(stream)
-    wsp, wsn = _ws_args(_lib.grouped_fp8_einsum_workspace_size(M, G, K, N), dev, sp, workspace)
+    wsp, wsn = _ws_args(_lib.grouped_fp8_einsum_workspace_size(kind, M, G, K, N), dev, sp, workspace)
     _check(_lib.grouped_fp8_einsum(kind, xp, ldx, xsfp, ldxsf, M, G, K, N, _ptr(w), _ptr(w_sf),
                                    _ptr(z_q), z_q.stride(0) if z_q is not None else 0,
                                    _ptr(z_sf), z_sf.stride(0) if z_sf is not None else 0,
@@ -247,7 +247,7 @@ def fp8_gemm_nt(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_s
         d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     _rows(d, torch.bfloat16, "d")
     sp = _stream(stream)
-    wsp, wsn = _ws_args(_lib.fp8_gemm_nt_workspace_size(M, N, K), a.device, sp, workspace)
+    wsp, wsn = _ws_args(_lib.fp8_gemm_nt_workspace_size(kind, M, N, K), a.device, sp, workspace)
     _check(_lib.fp8_gemm_nt(kind, ap, lda, asfp, ldasf, M, N, K, _ptr(b), _ptr(b_sf), _ptr(d), d.stride(0),
                             wsp, wsn, sp), "fp8_gemm_nt")
     return d

@@ -89,11 +89,31 @@ int bind_workspace(const mx::GemmPlan& plan, void* ws, int64_t ws_bytes, mx::Gem
   r = Range{};
   if (plan.workspace_bytes == 0) return MXFP8_OK;
   if (!ws || ws_bytes < plan.workspace_bytes || !aligned(ws, 256)) return MXFP8_ERR_WORKSPACE;
-  p.ws_counters = static_cast<uint32_t*>(ws);
-  p.ws_partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.counter_bytes);
+  if (plan.counter_bytes) {
+    p.ws_counters = static_cast<uint32_t*>(ws);
+    p.ws_partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.counter_bytes);
+  }
   r.lo = reinterpret_cast<uintptr_t>(ws);
   r.hi = r.lo + (uintptr_t)plan.workspace_bytes;
   return MXFP8_OK;
+}
+
+// Launches the GEMM of p.  BF16 activations that the plan routes to the tile
+// kernel are first quantized with the standalone quantizer into the workspace
+// (codes [M][kt], scales [M][kt/128]); the tile kernel then reads those, so the
+// result is the one pre-quantized activations give.
+hipError_t launch(mx::GemmArgs p, const mx::GemmPlan& plan, int64_t G, bool x_bf16, int out, void* ws,
+                  hipStream_t stream) {
+  if (x_bf16 && !plan.skinny) {
+    const int64_t kt = G * p.K;
+    uint8_t* q = static_cast<uint8_t*>(ws) + plan.stage_offset;
+    int32_t* sf = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + plan.stage_sf_offset);
+    const hipError_t e = mx::launch_quantize(p.x, p.M, kt, p.ld_x, q, kt, sf, kt / 128, stream);
+    if (e != hipSuccess) return e;
+    p.x = q; p.ld_x = kt; p.x_sf = sf; p.ld_xsf = kt / 128;
+    x_bf16 = false;
+  }
+  return mx::launch_gemm(p, G, x_bf16, out, stream);
 }
 
 }  // namespace
@@ -175,7 +195,8 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
   mx::GemmArgs p{};
   p.splitk_mode = g_splitk_mode.load(std::memory_order_relaxed);
   Range rw;
-  if (int s = bind_workspace(mx::plan_gemm(M, G, N, K), workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
+  const mx::GemmPlan plan = mx::plan_gemm(M, G, N, K, x_kind == MXFP8_ACT_BF16);
+  if (int s = bind_workspace(plan, workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
   for (const Range& o : outs)
     if (overlaps(rw, o)) return MXFP8_ERR_ALIAS;
   for (const Range& in : ins)
@@ -189,7 +210,7 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
   p.zsf = reinterpret_cast<uint8_t*>(z_sf); p.ld_zsf_bytes = ld_zsf * 4;
   p.zb = static_cast<uint16_t*>(z_bf16); p.ld_zb = ld_zb;
   const int out = (want_bf ? 1 : 0) | (want_mx ? 2 : 0);
-  const hipError_t e = mx::launch_gemm(p, G, x_kind == MXFP8_ACT_BF16, out, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch(p, plan, G, x_kind == MXFP8_ACT_BF16, out, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
@@ -214,7 +235,8 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
   mx::GemmArgs p{};
   p.splitk_mode = g_splitk_mode.load(std::memory_order_relaxed);
   Range rw;
-  if (int s = bind_workspace(mx::plan_gemm(M, 1, N, K), workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
+  const mx::GemmPlan plan = mx::plan_gemm(M, 1, N, K, a_kind == MXFP8_ACT_BF16);
+  if (int s = bind_workspace(plan, workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
   if (overlaps(rw, out)) return MXFP8_ERR_ALIAS;
   for (const Range& in : ins)
     if (overlaps(rw, in)) return MXFP8_ERR_ALIAS;
@@ -224,18 +246,20 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
   p.w = static_cast<const uint8_t*>(b); p.w_sf = b_sf;
   p.M = M; p.N = N; p.K = K;
   p.zb = static_cast<uint16_t*>(d); p.ld_zb = ld_d;
-  const hipError_t e = mx::launch_gemm(p, 1, a_kind == MXFP8_ACT_BF16, 1, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch(p, plan, 1, a_kind == MXFP8_ACT_BF16, 1, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
-MX_API int64_t grouped_fp8_einsum_workspace_size(int64_t M, int64_t G, int64_t K, int64_t N) {
+MX_API int64_t grouped_fp8_einsum_workspace_size(int x_kind, int64_t M, int64_t G, int64_t K, int64_t N) {
+  if (x_kind != MXFP8_ACT_BF16 && x_kind != MXFP8_ACT_MXFP8) return -1;
   if (M < 0 || G < 1 || G > 65535 || K <= 0 || K % 128 || N <= 0 || N % 128) return -1;
   if (K > kMaxDepth || M > INT32_MAX || G * N > INT32_MAX) return -1;
-  return mx::plan_gemm(M, G, N, K).workspace_bytes;
+  return mx::plan_gemm(M, G, N, K, x_kind == MXFP8_ACT_BF16).workspace_bytes;
 }
 
-MX_API int64_t fp8_gemm_nt_workspace_size(int64_t M, int64_t N, int64_t K) {
+MX_API int64_t fp8_gemm_nt_workspace_size(int a_kind, int64_t M, int64_t N, int64_t K) {
+  if (a_kind != MXFP8_ACT_BF16 && a_kind != MXFP8_ACT_MXFP8) return -1;
   if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return -1;
   if (K > kMaxDepth || M > INT32_MAX || N > INT32_MAX) return -1;
-  return mx::plan_gemm(M, 1, N, K).workspace_bytes;
+  return mx::plan_gemm(M, 1, N, K, a_kind == MXFP8_ACT_BF16).workspace_bytes;
 }

@@ -4,21 +4,12 @@
 // weights from HBM once (vLLM PR #60118 "[Perf][DSv4.1] MegaAttn: wo_a writes
 // wo_b's MXFP8 input", Claims: the decode range is 1-256 tokens).  HBM streams
 // near its peak only when every CU keeps many reads in flight for the whole
-// kernel, so the grid is sized to be resident in one round (two workgroups per
+// kernel, so the grid is sized to be resident in one round (one workgroup per
 // CU) and every workgroup streams a long K range through a software pipeline.
 //
 // Work item: 64 weight rows (two MFMA row tiles) x one chunk of up to 64 tokens
 // x one K range (split s of S).  Four waves: wave (rt, tt) owns the 32 x 32
 // output tile of row tile rt and token tile tt.
-//
-// Pipeline: K is walked in super-steps of two 128-deep steps.  All 256 threads
-// load a super-step's weight and activation tiles (64 rows x 256 bytes each,
-// 16 KB + 16 KB, row-contiguous 16-byte loads) into registers; two super-steps
-// are in flight while the MFMAs of a third read LDS.  Registers go to one of two
-// LDS buffers in the fragment-major layout of the LDS-tiled kernel (conflict-free
-// fragment reads), one barrier per super-step.  BF16 activations are quantized on
-// their way into LDS (the four lanes of a 32-block exchange their maxima, the
-// standalone quantizer's rule).
 //
 // Split K: with S > 1 every work item writes its fp32 partial tile to the
 // caller's workspace, and the last of the S items of a tile to arrive (an atomic
@@ -29,7 +20,6 @@
 
 namespace mx {
 
-
 namespace {
 
 constexpr uint32_t kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked
@@ -38,127 +28,6 @@ constexpr int kL2 = 0x01;                    // sc0: through L1 to the XCD's L2 
 constexpr int kLocalMaxSplits = 16;          // per-XCD arrival counts are 4-bit fields
 constexpr int kTileRows = 64;                // weight rows per work item
 constexpr int kChunkTokens = 64;             // tokens per work item (two token tiles)
-constexpr int kStepBytes = 64 * 128;         // one 128-deep step of a 64-row operand tile
-constexpr int kSuper = 2;                    // steps per super-step
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
-}
-
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
-  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
-
-// Fragment-major LDS layout of one 64-row step tile (see gemm_tiled.hip).
-__device__ __forceinline__ int frag_off(int r, int c) {
-  const int T = r >> 5, i = r & 31, KS = c >> 2, h = (c >> 1) & 1, q = c & 1;
-  return (((T * 2 + KS) * 2 + h) * 64 + ((i + 32 * q) ^ (8 * q))) * 16;
-}
-
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int T, int KS, int lane, int q) {
-  const uint8_t* b = tile + ((T * 2 + KS) * 2) * 1024 + (lane ^ (8 * q)) * 16;
-  return frag(*reinterpret_cast<const uint4*>(b), *reinterpret_cast<const uint4*>(b + 1024));
-}
-
-// Registers of one super-step in flight.  Weights and E4M3 activations: thread t
-// of instruction u covers row 8(4u + wave) + (lane & 7), chunk lane >> 3 of step
-// u / 8 (u < 16 over both steps: 64 rows x 8 chunks x 2 steps / 256 threads = 4 per
-// thread per operand).  BF16 activations: 64 rows x 2 steps x 16 chunks / 256 = 8.
-template <bool X_BF16>
-struct Super {
-  uint4 w[4];
-  uint4 x[X_BF16 ? 8 : 4];
-  uint32_t wsf;   // scale word: weight row (tid & 63), step (tid >> 6) & 1
-  uint32_t xsf;   // scale word: token row (tid & 63), step (tid >> 6) & 1 (E4M3 activations)
-};
-
-struct Ctx {
-  __amdgpu_buffer_rsrc_t rw, rws, rx, rxs;
-  int K, ksteps, ld_x_bytes, ld_xsf_bytes, xcol0, xsfcol0;
-  int k_lo, k_hi;         // this item's steps [k_lo, k_hi)
-  int m_rows;             // valid token rows of the chunk; rows past it load row m_rows - 1 and are zeroed
-};
-
-// Step index j of super-step `ss`, clamped into the item's range (loads of a step
-// past the range fetch a valid step; its MFMAs are skipped).
-__device__ __forceinline__ int step_of(const Ctx& c, int ss, int j) {
-  const int k = c.k_lo + ss * kSuper + j;
-  return k < c.k_hi ? k : c.k_hi - 1;
-}
-
-template <bool X_BF16>
-__device__ __forceinline__ void load_super(Super<X_BF16>& st, const Ctx& c, int ss, int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
-    st.w[u] = bload16(c.rw, row * c.K + step_of(c, ss, j) * 128 + ch * 16);
-  }
-  {
-    const int row = tid & 63, j = (tid >> 6) & 1;
-    st.wsf = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(c.rws, (row * c.ksteps + step_of(c, ss, j)) * 4, 0, 0);
-  }
-  if constexpr (!X_BF16) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
-      const int rc = row < c.m_rows ? row : c.m_rows - 1;
-      const uint4 v = bload16(c.rx, rc * c.ld_x_bytes + c.xcol0 + step_of(c, ss, j) * 128 + ch * 16);
-      st.x[u] = row < c.m_rows ? v : make_uint4(0, 0, 0, 0);
-    }
-    const int row = tid & 63, j = (tid >> 6) & 1, rc = row < c.m_rows ? row : c.m_rows - 1;
-    const uint32_t sv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-        c.rxs, rc * c.ld_xsf_bytes + c.xsfcol0 + step_of(c, ss, j) * 4, 0, 0);
-    st.xsf = row < c.m_rows ? sv : 0u;
-  } else {
-    // instruction u: step u >> 2, rows 16 * ((4 * (u & 3) + wave) >> 2) + (lane & 15), block
-    // (4 * (u & 3) + wave) & 3; lanes l, l+16, l+32, l+48 hold the block's four parts
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = u >> 2, k = 4 * (u & 3) + wave, rg = k >> 2, b = k & 3;
-      const int row = 16 * rg + (lane & 15), jj = 4 * b + (lane >> 4);
-      const int rc = row < c.m_rows ? row : c.m_rows - 1;
-      const uint4 v = bload16(c.rx, rc * c.ld_x_bytes + c.xcol0 + step_of(c, ss, j) * 256 + jj * 16);
-      st.x[u] = row < c.m_rows ? v : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-template <bool X_BF16>
-__device__ __forceinline__ void store_super(const Super<X_BF16>& st, uint8_t* sW, uint8_t* sX, uint32_t* sWs,
-                                            uint32_t* sXs, int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
-    *reinterpret_cast<uint4*>(sW + j * kStepBytes + frag_off(row, ch)) = st.w[u];
-  }
-  sWs[((tid >> 6) & 1) * 64 + (tid & 63)] = st.wsf;   // waves 2, 3 repeat waves 0, 1: same values
-  if constexpr (!X_BF16) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = u >> 1, row = 8 * (4 * (u & 1) + wave) + (lane & 7), ch = lane >> 3;
-      *reinterpret_cast<uint4*>(sX + j * kStepBytes + frag_off(row, ch)) = st.x[u];
-    }
-    sXs[((tid >> 6) & 1) * 64 + (tid & 63)] = st.xsf;
-  } else {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = u >> 2, k = 4 * (u & 3) + wave, rg = k >> 2, b = k & 3;
-      const int row = 16 * rg + (lane & 15), part = lane >> 4, jj = 4 * b + part;
-      const uint4 v = st.x[u];
-      uint32_t am = fold_pair(amax_pair(amax_pair(amax_pair(amax_pair(0u, v.x), v.y), v.z), v.w));
-      am = max(am, (uint32_t)__shfl_xor((int)am, 16));
-      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-      const int e = scale_exp_from_amax(am);
-      const float sc = exp2_int(e);
-      const uint2 codes = make_uint2(encode4(v.x, v.y, sc), encode4(v.z, v.w, sc));
-      *reinterpret_cast<uint2*>(sX + j * kStepBytes + frag_off(row, jj >> 1) + 8 * (jj & 1)) = codes;
-      if (part == 0) reinterpret_cast<uint8_t*>(sXs)[(j * 64 + row) * 4 + b] = (uint8_t)(e + 127);
-    }
-  }
-}
 
 }  // namespace
 
@@ -228,88 +97,10 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, const v16f& acc, 
   if (tid == 0) __hip_atomic_store(&p.ws_counters[tc], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-template <int MT, bool X_BF16, int OUT>
-__global__ __launch_bounds__(kThreads) void splitk_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sW[2][kSuper * kStepBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sX[2][kSuper * kStepBytes];
-  __shared__ uint32_t sWs[2][kSuper * 64];
-  __shared__ uint32_t sXs[2][kSuper * 64];
-  __shared__ int s_last;
-
-  const int total = G * n_tiles * chunks * S;
-  const int wi = xcd_work_index((int)blockIdx.x, total);
-  const int s = wi % S;
-  const int rest = wi / S;
-  const int chunk = rest % chunks;
-  const int tile = rest / chunks;
-  const int g = tile / n_tiles, nt = tile % n_tiles;
-  const int tc = tile * chunks + chunk;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, q = lane >> 5;
-  const int rt = wave & 1, tt = wave >> 1;
-
-  Ctx c;
-  c.K = (int)p.K;
-  c.ksteps = (int)(p.K / 128);
-  c.k_lo = (int)((int64_t)s * c.ksteps / S);
-  c.k_hi = (int)((int64_t)(s + 1) * c.ksteps / S);
-  const int nss = (c.k_hi - c.k_lo + kSuper - 1) / kSuper;
-  const int xes = X_BF16 ? 2 : 1;
-  c.ld_x_bytes = (int)(p.ld_x * xes);
-  c.ld_xsf_bytes = (int)(p.ld_xsf * 4);
-  c.xcol0 = (int)((int64_t)g * p.K * xes);
-  c.xsfcol0 = g * c.ksteps * 4;
-  const int64_t n_row0 = (int64_t)g * p.N + (int64_t)nt * kTileRows;
-  const int64_t m_first = (int64_t)chunk * kChunkTokens;
-  const int64_t m_rows = p.M - m_first < kChunkTokens ? p.M - m_first : kChunkTokens;
-  c.m_rows = (int)m_rows;
-  c.rw = make_rsrc(p.w + n_row0 * p.K, (int64_t)kTileRows * p.K);
-  c.rws = make_rsrc(p.w_sf + n_row0 * c.ksteps, (int64_t)kTileRows * c.ksteps * 4);
-  c.rx = make_rsrc(static_cast<const uint8_t*>(p.x) + m_first * c.ld_x_bytes,
-                   (m_rows - 1) * c.ld_x_bytes + (int64_t)G * p.K * xes);
-  c.rxs = X_BF16 ? c.rx
-                 : make_rsrc(p.x_sf + m_first * p.ld_xsf, ((m_rows - 1) * p.ld_xsf + (int64_t)G * c.ksteps) * 4);
-
-  v16f acc = zero16();
-  const bool computes = tt < MT;
-
-  Super<X_BF16> st0, st1;
-  load_super<X_BF16>(st0, c, 0, tid);
-  if (nss > 1) load_super<X_BF16>(st1, c, 1, tid);
-
-  // One super-step: the older registers in flight go to LDS buffer b, the next
-  // loads reuse them, and the MFMAs read buffer b.
-  auto body = [&](Super<X_BF16>& st, int ss, int b) {
-    store_super<X_BF16>(st, sW[b], sX[b], sWs[b], sXs[b], tid);
-    lds_barrier();
-    if (ss + 2 < nss) load_super<X_BF16>(st, c, ss + 2, tid);
-    if (computes) {
-#pragma unroll
-      for (int j = 0; j < kSuper; ++j) {
-        if (c.k_lo + ss * kSuper + j < c.k_hi) {
-          const uint8_t* tw = sW[b] + j * kStepBytes;
-          const uint8_t* tx = sX[b] + j * kStepBytes;
-          const int sw = (int)(sWs[b][j * 64 + rt * 32 + i] >> (8 * q));
-          const int sx = (int)(sXs[b][j * 64 + tt * 32 + i] >> (8 * q));
-          acc = mfma_scaled<0>(read_frag(tw, rt, 0, lane, q), read_frag(tx, tt, 0, lane, q), acc, sw, sx);
-          acc = mfma_scaled<2>(read_frag(tw, rt, 1, lane, q), read_frag(tx, tt, 1, lane, q), acc, sw, sx);
-        }
-      }
-    }
-  };
-  for (int ss = 0; ss < nss; ss += 2) {
-    body(st0, ss, 0);
-    if (ss + 1 < nss) body(st1, ss + 1, 1);
-  }
-
-  finish_tile<MT, OUT>(p, acc, tc, s, S, rt, tt, lane, tid, n_row0 + rt * 32, m_first + tt * 32 + i, computes,
-                       &s_last);
-}
-
 // ---------------------------------------------------------------------------
-// E4M3 activations: the weight-streaming kernel proper.
+// The weight-streaming kernel.
 //
-// Both operands are codes, so every byte goes from memory straight into LDS
+// E4M3 activations: both operands are codes, so every byte goes from memory straight into LDS
 // (buffer_load ... lds) and the pipeline depth is bounded by LDS, not registers:
 // a ring of kRing stages of kStageSteps 128-deep steps (64 weight rows and 64 token
 // rows x 128 bytes per step: 32 KB per stage), with the loads of stage t + kRing - 1
@@ -325,9 +116,10 @@ __global__ __launch_bounds__(kThreads) void splitk_kernel(GemmArgs p, int G, int
 // 128-byte reads), and the 16 (or 8) lanes of a fragment read -- 16 rows, one
 // chunk -- hit distinct 16-byte bank groups.  Scale tables: row r holds the words
 // of steps k_lo .. k_lo + 31 as eight 16-byte chunks, chunk c at position c ^ (r & 7).
-// A lane's fragment (row i, chunks 4KS + q and 4KS + 2 + q) is the same bytes in
-// the same MFMA order as in the register-staged kernel above, which uses the same
-// split plan, so E4M3 and BF16 activations give identical bits.
+// A lane's fragment is row i, chunks 4KS + q and 4KS + 2 + q.  BF16 activations
+// take the same path with the activation slot of each stage filled by the
+// workgroup's own threads (quantized in registers), so E4M3 and BF16 activations
+// give identical bits.
 constexpr int kRing = 4;
 constexpr int kStageSteps = 2;
 constexpr int kMaxSteps = 32;
@@ -657,13 +449,6 @@ template <int MT, int OUT, bool XB>
 static hipError_t launch_stream(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
   hipLaunchKernelGGL((stream_kernel<MT, OUT, XB>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p, (int)G,
                      plan.n_tiles, plan.chunks, plan.splits);
-  return hipGetLastError();
-}
-
-template <int MT, bool X_BF16, int OUT>
-static hipError_t launch_mt(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  hipLaunchKernelGGL((splitk_kernel<MT, X_BF16, OUT>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream,
-                     p, (int)G, plan.n_tiles, plan.chunks, plan.splits);
   return hipGetLastError();
 }
 

@@ -1,71 +1,28 @@
-// Block-scaled FP8 GEMM for many tokens (prefill): LDS-tiled, double-buffered,
-// on gfx950's V_MFMA_SCALE_F32_32X32X64_F8F6F4.
+// Block-scaled FP8 GEMM for many tokens (prefill) on gfx950's
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4, both operands direct to LDS.
 //
-// One kernel family serves both projections of the o_proj chain:
+// One kernel serves both projections of the o_proj chain:
 //   * grouped_fp8_einsum (wo_a): G groups, z[m, g*N+n] = sum_k x[m, g*K+k] w[g,n,k],
 //     epilogue writes z as BF16 and/or MXFP8 (vLLM PR #60118 "[Perf][DSv4.1]
 //     MegaAttn: wo_a writes wo_b's MXFP8 input", Overview and Claims);
 //   * fp8_gemm_nt (wo_b): G = 1, BF16 output, recipe (1,1,32) (vLLM PR #57977
 //     "[Perf][DSv4.1] Keep activations MXFP8 between DeepGEMM kernels", Pieces).
-// Activations arrive either pre-quantized (codes + packed scales) or as BF16,
-// which the load path quantizes with the same rule as mxfp8_quantize (PR #57977,
-// Test Result: pre-quantized input is bit-identical to in-kernel quantization).
+// The kernel reads E4M3 activations (codes + packed scales); the library
+// quantizes BF16 activations with mxfp8_quantize first (into the caller's
+// workspace), so both kinds give identical bits (PR #57977, Test Result).
 //
 // Tiling.  A workgroup of four waves owns BN weight rows x BM tokens and walks K
-// in steps of 128 bytes (exactly one packed scale word per row and step).  Wave
-// (wn, wm) owns a (BN / WAVES_N) x (BM / WAVES_M) sub-tile of 32 x 32 MFMA tiles,
-// so one step is 2 * TN * TM scaled MFMAs per wave.  Both operand tiles of a step
-// live in LDS, twice (double buffer): while the MFMAs of step k read one buffer,
-// the loads of step k+1 are in flight into registers and are written into the
-// other buffer afterwards, so one barrier per step suffices.
+// in 64-deep half steps.  Wave (wn, wm) owns a (BN / WAVES_N) x (BM / WAVES_M)
+// sub-tile of 32 x 32 MFMA tiles, TN x TM of them.
 //
-// LDS layout ("fragment-major").  An MFMA operand fragment is the 32 bytes lane
-// l = i + 32q needs for one 64-deep half KS of a step: chunks 4KS + q and
-// 4KS + 2 + q (16 bytes each) of tile row 32T + i.  Chunk c of row r is stored at
-//     16 * (64 * ((2T + KS) * 2 + h) + ((i + 32q) ^ 8q)),  KS = c/4, h = (c/2)%2, q = c%2,
-// so a wave reads one fragment half with one ds_read_b128 over 64 consecutive
-// 16-byte slots (bank-conflict free), and the 8 rows x 8 chunks one global-load
-// instruction brings in land in distinct bank groups when written.
-//
-// Token rows past M: the register-staged kernel loads a valid row instead and
-// zeroes the value (code 0; BF16 zero quantizes to code 0 with scale byte 0); the
-// direct-to-LDS kernel keeps the row part of every offset in the per-lane
+// Token rows past M: the row part of every activation offset is in the per-lane
 // register, which the buffer range check covers (the scalar offset is not
-// checked), and sets the range to end at row M, so those rows arrive as zeros.
+// checked), and the range ends at row M, so those rows arrive as zeros.
 #include <type_traits>
 
 #include "gemm_common.hpp"
 
 namespace mx {
-
-
-constexpr uint32_t kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords, range-checked
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
-}
-
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
-  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
-
-__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-
-// Byte offset of 16-byte chunk c (0..7) of tile row r in the fragment-major layout.
-__device__ __forceinline__ int frag_off(int r, int c) {
-  const int T = r >> 5, i = r & 31, KS = c >> 2, h = (c >> 1) & 1, q = c & 1;
-  return (((T * 2 + KS) * 2 + h) * 64 + ((i + 32 * q) ^ (8 * q))) * 16;
-}
-
-// The fragment of MFMA row tile T, 64-deep half KS, for lane l (q = l / 32).
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int T, int KS, int lane, int q) {
-  const int slot = lane ^ (8 * q);
-  const uint8_t* b = tile + ((T * 2 + KS) * 2) * 1024 + slot * 16;
-  return frag(*reinterpret_cast<const uint4*>(b), *reinterpret_cast<const uint4*>(b + 1024));
-}
 
 template <int BN_, int BM_, int WAVES_N_, int WAVES_M_>
 struct BigCfg {
@@ -74,209 +31,10 @@ struct BigCfg {
   static constexpr int WN = BN / WAVES_N, WM = BM / WAVES_M;
   static constexpr int TN = WN / 32, TM = WM / 32;
   static_assert(WN % 32 == 0 && WM % 32 == 0, "32-row MFMA tiles");
-  static constexpr int W_LOADS = BN * 8 / THREADS;       // 16-byte weight chunks per thread and step
-  static constexpr int XQ_LOADS = BM * 8 / THREADS;      // 16-byte E4M3 activation chunks
-  static constexpr int XB_LOADS = BM * 16 / THREADS;     // 16-byte BF16 activation chunks
-  static_assert(W_LOADS * THREADS == BN * 8 && XQ_LOADS * THREADS == BM * 8 && XB_LOADS * THREADS == BM * 16,
-                "load mapping");
-  static_assert(THREADS % BN == 0 && THREADS % BM == 0, "scale words: every row covered by a thread");
 };
-
-template <class C, bool X_BF16>
-struct Stage {
-  uint4 w[C::W_LOADS];
-  uint4 x[X_BF16 ? C::XB_LOADS : C::XQ_LOADS];
-  uint32_t wsf;   // scale word of weight row tid % BN
-  uint32_t xsf;   // scale word of token row tid % BM (E4M3 activations)
-};
-
-template <class C, bool X_BF16>
-__device__ __forceinline__ void load_stage(Stage<C, X_BF16>& st, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rws,
-                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rxs, int64_t K,
-                                           int ksteps, int ld_x_bytes, int ld_xsf_bytes, int xcol0, int xsfcol0,
-                                           int kt, int tid, int m_rows) {
-  const int wave = tid >> 6, lane = tid & 63;
-  // weights: instruction u of wave w covers rows 8(4u + w) .. +7, all 8 chunks of the step
-#pragma unroll
-  for (int u = 0; u < C::W_LOADS; ++u) {
-    const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
-    st.w[u] = bload16(rw, row * (int)K + kt * 128 + c * 16);
-  }
-  st.wsf = bload4(rws, ((tid % C::BN) * ksteps + kt) * 4);
-  if constexpr (!X_BF16) {
-#pragma unroll
-    for (int u = 0; u < C::XQ_LOADS; ++u) {
-      const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
-      const int rc = row < m_rows ? row : m_rows - 1;
-      const uint4 v = bload16(rx, rc * ld_x_bytes + xcol0 + kt * 128 + c * 16);
-      st.x[u] = row < m_rows ? v : make_uint4(0, 0, 0, 0);
-    }
-    const int srow = tid % C::BM, src = srow < m_rows ? srow : m_rows - 1;
-    const uint32_t sv = bload4(rxs, src * ld_xsf_bytes + xsfcol0 + kt * 4);
-    st.xsf = srow < m_rows ? sv : 0u;
-  } else {
-    // BF16: instruction u covers 16 rows x one 32-element block b; the four lanes
-    // l, l+16, l+32, l+48 hold the block's four 16-byte parts.
-#pragma unroll
-    for (int u = 0; u < C::XB_LOADS; ++u) {
-      const int k = C::NW * u + wave, rg = k >> 2, b = k & 3;
-      const int row = 16 * rg + (lane & 15), jj = 4 * b + (lane >> 4);
-      const int rc = row < m_rows ? row : m_rows - 1;
-      const uint4 v = bload16(rx, rc * ld_x_bytes + xcol0 + kt * 256 + jj * 16);
-      st.x[u] = row < m_rows ? v : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-template <class C, bool X_BF16>
-__device__ __forceinline__ void store_stage(const Stage<C, X_BF16>& st, uint8_t* sW, uint8_t* sX, uint32_t* sWs,
-                                            uint32_t* sXs, int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int u = 0; u < C::W_LOADS; ++u) {
-    const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
-    *reinterpret_cast<uint4*>(sW + frag_off(row, c)) = st.w[u];
-  }
-  sWs[tid % C::BN] = st.wsf;        // threads past BN repeat a row's word: same value, same slot
-  if constexpr (!X_BF16) {
-#pragma unroll
-    for (int u = 0; u < C::XQ_LOADS; ++u) {
-      const int row = 8 * (C::NW * u + wave) + (lane & 7), c = lane >> 3;
-      *reinterpret_cast<uint4*>(sX + frag_off(row, c)) = st.x[u];
-    }
-    sXs[tid % C::BM] = st.xsf;
-  } else {
-#pragma unroll
-    for (int u = 0; u < C::XB_LOADS; ++u) {
-      const int k = C::NW * u + wave, rg = k >> 2, b = k & 3;
-      const int row = 16 * rg + (lane & 15), part = lane >> 4, jj = 4 * b + part;
-      const uint4 v = st.x[u];
-      uint32_t am = fold_pair(amax_pair(amax_pair(amax_pair(amax_pair(0u, v.x), v.y), v.z), v.w));
-      am = max(am, (uint32_t)__shfl_xor((int)am, 16));
-      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-      const int e = scale_exp_from_amax(am);
-      const float sc = exp2_int(e);
-      const uint2 codes = make_uint2(encode4(v.x, v.y, sc), encode4(v.z, v.w, sc));
-      *reinterpret_cast<uint2*>(sX + frag_off(row, jj >> 1) + 8 * (jj & 1)) = codes;
-      if (part == 0) reinterpret_cast<uint8_t*>(sXs)[row * 4 + b] = (uint8_t)(e + 127);
-    }
-  }
-}
-
-// One 128-deep step of a wave's sub-tile: two 64-deep halves of TN x TM scaled MFMAs.
-template <class C>
-__device__ __forceinline__ void mma_step(v16f (&acc)[C::TN][C::TM], const uint8_t* sW, const uint8_t* sX,
-                                         const uint32_t* sWs, const uint32_t* sXs, int wn, int wm, int lane, int q,
-                                         int i) {
-  int sw[C::TN], sx[C::TM];
-#pragma unroll
-  for (int a = 0; a < C::TN; ++a) sw[a] = (int)(sWs[(wn * C::TN + a) * 32 + i] >> (8 * q));
-#pragma unroll
-  for (int b = 0; b < C::TM; ++b) sx[b] = (int)(sXs[(wm * C::TM + b) * 32 + i] >> (8 * q));
-  {
-    v8i fw[C::TN], fx[C::TM];
-#pragma unroll
-    for (int a = 0; a < C::TN; ++a) fw[a] = read_frag(sW, wn * C::TN + a, 0, lane, q);
-#pragma unroll
-    for (int b = 0; b < C::TM; ++b) fx[b] = read_frag(sX, wm * C::TM + b, 0, lane, q);
-#pragma unroll
-    for (int a = 0; a < C::TN; ++a)
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<0>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
-  }
-#ifdef MX_KS_BARRIER
-  __builtin_amdgcn_sched_barrier(0);
-#endif
-  {
-    v8i fw[C::TN], fx[C::TM];
-#pragma unroll
-    for (int a = 0; a < C::TN; ++a) fw[a] = read_frag(sW, wn * C::TN + a, 1, lane, q);
-#pragma unroll
-    for (int b = 0; b < C::TM; ++b) fx[b] = read_frag(sX, wm * C::TM + b, 1, lane, q);
-#pragma unroll
-    for (int a = 0; a < C::TN; ++a)
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2>(fw[a], fx[b], acc[a][b], sw[a], sx[b]);
-  }
-}
-
-template <class C, bool X_BF16, int OUT>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
-void big_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sW[2][C::BN * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sX[2][C::BM * 128];
-  __shared__ uint32_t sWs[2][C::BN];
-  __shared__ uint32_t sXs[2][C::BM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 5, i = lane & 31;
-  const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
-
-  const int total = G * m_tiles * n_tiles;
-  const int wi = xcd_work_index((int)blockIdx.x, total);
-  const int nt = wi % n_tiles;
-  const int rest = wi / n_tiles;
-  const int mt = rest % m_tiles;
-  const int g = rest / m_tiles;
-
-  const int64_t n0 = (int64_t)nt * C::BN;                 // within the group
-  const int64_t m0 = (int64_t)mt * C::BM;
-  const int ksteps = (int)(p.K / 128);
-  const int64_t rows_left = p.M - m0;
-  const int64_t m_rows = rows_left < C::BM ? rows_left : C::BM;
-
-  const int xes = X_BF16 ? 2 : 1;
-  const int ld_x_bytes = (int)(p.ld_x * xes);
-  const int ld_xsf_bytes = (int)(p.ld_xsf * 4);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + ((int64_t)g * p.N + n0) * p.K, (int64_t)C::BN * p.K);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_sf + ((int64_t)g * p.N + n0) * ksteps, (int64_t)C::BN * ksteps * 4);
-  const __amdgpu_buffer_rsrc_t rx =
-      make_rsrc(static_cast<const uint8_t*>(p.x) + m0 * ld_x_bytes, (m_rows - 1) * ld_x_bytes + p.K * G * xes);
-  const __amdgpu_buffer_rsrc_t rxs =
-      X_BF16 ? rx : make_rsrc(p.x_sf + m0 * p.ld_xsf, ((m_rows - 1) * p.ld_xsf + G * ksteps) * 4);
-  const int xcol0 = (int)((int64_t)g * p.K * xes);
-  const int xsfcol0 = g * ksteps * 4;
-
-  v16f acc[C::TN][C::TM];
-#pragma unroll
-  for (int a = 0; a < C::TN; ++a)
-#pragma unroll
-    for (int b = 0; b < C::TM; ++b) acc[a][b] = zero16();
-
-  Stage<C, X_BF16> st;
-  load_stage<C, X_BF16>(st, rw, rws, rx, rxs, p.K, ksteps, ld_x_bytes, ld_xsf_bytes, xcol0, xsfcol0, 0, tid, (int)m_rows);
-  store_stage<C, X_BF16>(st, sW[0], sX[0], sWs[0], sXs[0], tid);
-  lds_barrier();
-
-  // Steps 0 .. ksteps-2 prefetch the next step; the last step is peeled off.
-  for (int kt = 0; kt + 1 < ksteps; ++kt) {
-    const int s = kt & 1;
-    load_stage<C, X_BF16>(st, rw, rws, rx, rxs, p.K, ksteps, ld_x_bytes, ld_xsf_bytes, xcol0, xsfcol0, kt + 1, tid, (int)m_rows);
-    // keep the order: loads in flight across the MFMAs, LDS stores after them
-    __builtin_amdgcn_sched_barrier(0);
-    mma_step<C>(acc, sW[s], sX[s], sWs[s], sXs[s], wn, wm, lane, q, i);
-    __builtin_amdgcn_sched_barrier(0);
-    store_stage<C, X_BF16>(st, sW[s ^ 1], sX[s ^ 1], sWs[s ^ 1], sXs[s ^ 1], tid);
-    lds_barrier();
-  }
-  {
-    const int s = (ksteps - 1) & 1;
-    mma_step<C>(acc, sW[s], sX[s], sWs[s], sXs[s], wn, wm, lane, q, i);
-  }
-
-  // ---- epilogue
-#pragma unroll
-  for (int b = 0; b < C::TM; ++b) {
-    const int64_t m = m0 + (wm * C::TM + b) * 32 + i;
-#pragma unroll
-    for (int a = 0; a < C::TN; ++a)
-      store_tile<OUT>(p, acc[a][b], m, m < p.M, (int64_t)g * p.N + n0 + (wn * C::TN + a) * 32, q);
-  }
-}
 
 // ---------------------------------------------------------------------------
-// E4M3 activations: direct-to-LDS variant.
-//
-// Both operands are already codes, so they go from memory straight into LDS
+// Both operands are codes, so they go from memory straight into LDS
 // (buffer_load_dwordx4 ... lds: lane l of an instruction writes 16 bytes at
 // LDS base + 16 l) and no registers stage them.  That frees enough LDS to keep
 // four half-step stages (64-deep: 256 rows x 64 bytes per operand = 16 KB), so
@@ -290,15 +48,9 @@ void big_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
 // each) fills 1 KB of consecutive slots, and the 16 lanes of one fragment read
 // (16 rows, one chunk) hit 16 different 16-byte bank groups (8 for any 8 rows).
 // The fragment of lane (i, q) is chunk q (dwords 0-3) and chunk 2 + q (dwords
-// 4-7) of row i: the same operand bytes, in the same MFMA order, as the
-// register-staged kernel above, so both kernels give identical bits.
+// 4-7) of row i: operand bytes 16q .. 16q+15 and 32+16q .. 32+16q+15 of the half
+// step, the MFMA's lane layout.
 __device__ __forceinline__ int dl_g(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
-
-__device__ __forceinline__ v8i dl_read_frag(const uint8_t* stage_op, int T, int lane) {
-  const int i = lane & 31, q = lane >> 5, gi = dl_g(i);
-  const uint8_t* b = stage_op + T * 2048 + 64 * i;
-  return frag(*reinterpret_cast<const uint4*>(b + 16 * (q ^ gi)), *reinterpret_cast<const uint4*>(b + 16 * ((2 + q) ^ gi)));
-}
 
 // LDS of the direct-to-LDS kernel: four half-step stages of operand data, then
 // two buffers of scale words.  A scale buffer holds the words of four K-steps
@@ -591,25 +343,10 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
   }
 }
 
-// Tile configurations.  The choice depends only on (M, G, N, K), never on the
-// activation kind or the output mode, so every variant of one shape shares the
-// accumulation order.
-using Cfg256 = BigCfg<256, 256, 2, 2>;   // E4M3 activations: 128 x 128 per wave
-using Cfg128 = BigCfg<128, 256, 1, 4>;   // E4M3 activations, N not a multiple of 256: 128 x 64 per wave
-// BF16 activations stage twice the bytes in registers and quantize them there:
-// half as many tokens per tile keeps the kernel within its registers (no spills).
-using CfgB256 = BigCfg<256, 128, 2, 2>;  // 128 x 64 per wave
-using CfgB128 = BigCfg<128, 128, 1, 4>;  // 128 x 32 per wave
-
-template <class C, bool X_BF16, int OUT>
-static hipError_t launch_cfg(const GemmArgs& p, int64_t G, hipStream_t stream) {
-  const int n_tiles = (int)(p.N / C::BN);
-  const int m_tiles = (int)((p.M + C::BM - 1) / C::BM);
-  const int64_t total = G * n_tiles * (int64_t)m_tiles;
-  hipLaunchKernelGGL((big_gemm_kernel<C, X_BF16, OUT>), dim3((unsigned)total), dim3(C::THREADS), 0, stream, p, (int)G,
-                     m_tiles, n_tiles);
-  return hipGetLastError();
-}
+// Tile configurations: 256 weight rows x 256 tokens; 128 x 256 when N is not a
+// multiple of 256.  The choice depends only on (G, N), never on the output mode.
+using Cfg256 = BigCfg<256, 256, 2, 2>;   // 128 x 128 per wave
+using Cfg128 = BigCfg<128, 256, 1, 4>;   // 128 x 64 per wave
 
 template <class C, int OUT>
 static hipError_t launch_dl(const GemmArgs& p, int64_t G, hipStream_t stream) {
@@ -621,29 +358,19 @@ static hipError_t launch_dl(const GemmArgs& p, int64_t G, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// E4M3 activations: the direct-to-LDS kernel; BF16 activations: the register-
-// staged kernel, which quantizes on the way into LDS.  Both feed the MFMAs the
-// same bytes in the same K order (an output element's value does not depend on
-// the tile that holds it), so pre-quantized and BF16 activations give identical bits.
-template <class CQ, class CB>
-static hipError_t dispatch_kind_out(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t s) {
-  if (x_bf16) {
-    if (out == OUT_BF16) return launch_cfg<CB, true, OUT_BF16>(p, G, s);
-    if (out == OUT_MX) return launch_cfg<CB, true, OUT_MX>(p, G, s);
-    return launch_cfg<CB, true, OUT_BOTH>(p, G, s);
-  }
-  if (out == OUT_BF16) return launch_dl<CQ, OUT_BF16>(p, G, s);
-  if (out == OUT_MX) return launch_dl<CQ, OUT_MX>(p, G, s);
-  return launch_dl<CQ, OUT_BOTH>(p, G, s);
+template <class C>
+static hipError_t dispatch_out(const GemmArgs& p, int64_t G, int out, hipStream_t s) {
+  if (out == OUT_BF16) return launch_dl<C, OUT_BF16>(p, G, s);
+  if (out == OUT_MX) return launch_dl<C, OUT_MX>(p, G, s);
+  return launch_dl<C, OUT_BOTH>(p, G, s);
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream) {
-  if (p.N % 256 == 0) return dispatch_kind_out<Cfg256, CfgB256>(p, G, x_bf16, out, stream);
-  return dispatch_kind_out<Cfg128, CfgB128>(p, G, x_bf16, out, stream);
+hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, int out, hipStream_t stream) {
+  if (p.N % 256 == 0) return dispatch_out<Cfg256>(p, G, out, stream);
+  return dispatch_out<Cfg128>(p, G, out, stream);
 }
 
-// Kernel choice between the few-token and the tiled family: a pure function of
-// (M, G, N, K) -- never of the activation kind or the output mode.
+// Few-token plan (the streaming kernel)
 constexpr int64_t kSkinnyMaxTokens = 256;
 // The few-token kernels are sized for one resident round: one workgroup per CU.
 constexpr int64_t kSkinnyTargetWorkgroups = 256;
@@ -653,7 +380,7 @@ constexpr int64_t kSkinnyMaxSteps = 32;       // 128-deep steps per split (the s
 // calls share a workspace.
 constexpr int64_t kCounterBytes = 65536;
 
-GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K) {
+GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
   GemmPlan pl{};
   const int mt = M <= 32 ? 1 : 2;
   const int64_t chunks = (M + 63) / 64;
@@ -661,7 +388,15 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K) {
   pl.skinny = M <= kSkinnyMaxTokens && tiles * 8 <= kCounterBytes;     // one 64-bit counter per tile
   if (!pl.skinny) {
     const int64_t bn = N % 256 == 0 ? 256 : 128;
-    pl.workgroups = G * (N / bn) * ((M + 255) / 256);     // E4M3 activations (BF16: twice as many)
+    pl.workgroups = G * (N / bn) * ((M + 255) / 256);
+    if (x_bf16 && M > 0) {
+      // the tile kernel reads E4M3 activations: BF16 ones are quantized first, into the workspace
+      // (after the counter region: a workspace shared with split-K calls keeps its counters)
+      const int64_t kt = G * K;
+      pl.stage_offset = kCounterBytes;
+      pl.stage_sf_offset = pl.stage_offset + (M * kt + 255) / 256 * 256;
+      pl.workspace_bytes = pl.stage_sf_offset + (M * (kt / 32) + 255) / 256 * 256;
+    }
     return pl;
   }
   const int64_t ksteps = K / 128;
@@ -684,9 +419,10 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream) {
   if (p.N % 128 != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
-  const GemmPlan plan = plan_gemm(p.M, G, p.N, p.K);
+  const GemmPlan plan = plan_gemm(p.M, G, p.N, p.K, x_bf16);
   if (plan.skinny) return launch_gemm_skinny(p, plan, G, x_bf16, out, stream);
-  return launch_gemm_tiled(p, G, x_bf16, out, stream);
+  if (x_bf16) return hipErrorInvalidValue;        // the caller quantizes into the workspace first
+  return launch_gemm_tiled(p, G, out, stream);
 }
 
 }  // namespace mx

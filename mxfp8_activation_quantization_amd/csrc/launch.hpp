@@ -35,7 +35,10 @@ struct GemmArgs {
 };
 
 // Kernel choice and scratch needs of one GEMM launch: a pure function of
-// (M, G, N, K).  `workspace_bytes` is 0 when no split-K reduction is needed.
+// (M, G, N, K, activation kind).  Workspace layout, each part 256-byte aligned:
+// split-K arrival counters, split-K fp32 partial tiles, then -- BF16 activations
+// with many tokens -- the activations quantized to MXFP8 (codes [M][G*K], scales
+// [M][G*K/128]).  `workspace_bytes` is 0 when nothing is needed.
 struct GemmPlan {
   bool skinny;
   int mt;                 // token tiles of 32 per workgroup (skinny)
@@ -43,11 +46,13 @@ struct GemmPlan {
   int n_tiles;            // 64-row weight tiles per group (skinny)
   int splits;             // K splits (skinny)
   int64_t workgroups;
-  int64_t counter_bytes;  // leading part of the workspace: one uint32 per (tile, chunk), 256-byte aligned
+  int64_t counter_bytes;  // leading part of the workspace: one 64-bit counter per (tile, chunk)
+  int64_t stage_offset;   // BF16 activations, many tokens: codes [M][G*K] at this offset
+  int64_t stage_sf_offset;//   and packed scales [M][G*K/128] at this one (0 when unused)
   int64_t workspace_bytes;
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K);
+GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16);
 
 hipError_t launch_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, void* q, int64_t ld_q,
                            int32_t* sf, int64_t ld_sf, hipStream_t stream);

@@ -140,8 +140,8 @@ def test_size_limits_of_tile_addressing():
     assert gemm(ld_asf=(1 << 16)) == B.MXFP8_ERR_SHAPE                      # scale rows: 4 bytes per word
     assert gemm(K=(1 << 22) + 128) == B.MXFP8_ERR_SHAPE
     assert einsum(K=(1 << 22) + 128) == B.MXFP8_ERR_SHAPE
-    assert LIB.fp8_gemm_nt_workspace_size(4, 256, (1 << 22) + 128) == -1
-    assert LIB.grouped_fp8_einsum_workspace_size(4, 2, (1 << 22) + 128, 128) == -1
+    assert LIB.fp8_gemm_nt_workspace_size(B.MXFP8_ACT_MXFP8, 4, 256, (1 << 22) + 128) == -1
+    assert LIB.grouped_fp8_einsum_workspace_size(B.MXFP8_ACT_MXFP8, 4, 2, (1 << 22) + 128, 128) == -1
 
 
 @pytest.mark.skipif(HAVE_GPU, reason="a GPU is present")
@@ -150,20 +150,27 @@ def test_valid_gemm_reports_missing_device():
 
 
 def test_workspace_sizes():
+    Q, BF = B.MXFP8_ACT_MXFP8, B.MXFP8_ACT_BF16
     # a K range shorter than two 256-deep super-steps per split is never split (no scratch); deeper K is
     # split across workgroups in the decode range only
-    assert LIB.grouped_fp8_einsum_workspace_size(64, 8, 512, 1024) == 0
-    need = LIB.grouped_fp8_einsum_workspace_size(64, 8, 4096, 1024)
+    assert LIB.grouped_fp8_einsum_workspace_size(Q, 64, 8, 512, 1024) == 0
+    need = LIB.grouped_fp8_einsum_workspace_size(Q, 64, 8, 4096, 1024)
     assert need > 0 and need % 256 == 0
-    assert LIB.fp8_gemm_nt_workspace_size(64, 5120, 8192) > 0
-    assert LIB.fp8_gemm_nt_workspace_size(4096, 5120, 8192) == 0        # many tokens: no split
-    assert LIB.fp8_gemm_nt_workspace_size(0, 5120, 8192) == 0
-    assert LIB.grouped_fp8_einsum_workspace_size(64, 8, 4000, 1024) == -1
-    assert LIB.fp8_gemm_nt_workspace_size(64, 100, 8192) == -1
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 64, 8, 4096, 1024) == need   # decode: quantized in the kernel
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 64, 5120, 8192) > 0
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 4096, 5120, 8192) == 0        # many tokens: no split
+    # many BF16 tokens: the activations are quantized into the workspace first (codes + packed scales),
+    # after the counter region that split-K calls sharing the workspace keep
+    assert LIB.fp8_gemm_nt_workspace_size(BF, 4096, 5120, 8192) == 65536 + 4096 * 8192 + 4096 * 8192 // 32
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 300, 8, 4096, 1024) >= 300 * 32768 * (1 + 1 / 32)
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 0, 5120, 8192) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(Q, 64, 8, 4000, 1024) == -1
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 64, 100, 8192) == -1
+    assert LIB.fp8_gemm_nt_workspace_size(7, 64, 128, 8192) == -1          # unknown activation kind
 
 
 def test_workspace_errors():
-    need = LIB.fp8_gemm_nt_workspace_size(4, 256, 4096)
+    need = LIB.fp8_gemm_nt_workspace_size(B.MXFP8_ACT_MXFP8, 4, 256, 4096)
     assert need > 0
     assert gemm(K=4096, ws=None) == B.MXFP8_ERR_WORKSPACE
     assert gemm(K=4096, ws_bytes=need - 1) == B.MXFP8_ERR_WORKSPACE

@@ -137,7 +137,7 @@ def test_split_k_workspace_counters_return_to_zero(lib):
     M, N, K = 48, 256, 4096
     aq, asf = exact_operands(rng, M, K)
     bq, bsf = exact_operands(rng, N, K)
-    need = B.lib().fp8_gemm_nt_workspace_size(M, N, K)
+    need = B.lib().fp8_gemm_nt_workspace_size(B.MXFP8_ACT_MXFP8, M, N, K)
     assert need > 0
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     outs = [lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(bq), i32_to_dev(bsf), workspace=ws)
@@ -165,8 +165,8 @@ def test_split_k_combine_modes_give_identical_bits(lib, kind, M, G, N, K):
         w_t, wsf_t = u8_to_dev(wq), i32_to_dev(wsf)
     else:
         w_t, wsf_t = u8_to_dev(wq.reshape(G, N, K)), i32_to_dev(wsf.reshape(G, N, K // 128))
-    need = (B.lib().fp8_gemm_nt_workspace_size(M, N, K) if kind == "gemm"
-            else B.lib().grouped_fp8_einsum_workspace_size(M, G, K, N))
+    need = (B.lib().fp8_gemm_nt_workspace_size(B.MXFP8_ACT_MXFP8, M, N, K) if kind == "gemm"
+            else B.lib().grouped_fp8_einsum_workspace_size(B.MXFP8_ACT_MXFP8, M, G, K, N))
     assert need > 0                                                       # the shape is split along K
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     outs = {}
@@ -388,13 +388,34 @@ def test_large_configs_sampled_rows(lib, name):
     _cases.pop(name)
 
 
+def test_bf16_staging_keeps_split_k_counters(lib):
+    """A BF16 call with many tokens (quantized into the workspace first) leaves the split-K counter region of a
+    shared workspace untouched, so a following decode-size split-K call on the same workspace stays exact."""
+    from mxfp8_activation_quantization_amd import binding as B
+    rng = np.random.default_rng(93)
+    Q, BF = B.MXFP8_ACT_MXFP8, B.MXFP8_ACT_BF16
+    need = max(B.lib().fp8_gemm_nt_workspace_size(BF, 300, 256, 2048),
+               B.lib().fp8_gemm_nt_workspace_size(Q, 48, 256, 4096))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    vals = rng.choice(EXACT_VALUES, size=(300, 2048)).astype(np.float32)
+    a_bf = bf16_to_dev(mx.bf16_round(vals))
+    bq, bsf = exact_operands(rng, 256, 2048)
+    lib.fp8_gemm_nt(a_bf, None, u8_to_dev(bq), i32_to_dev(bsf), workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+    aq, asf = exact_operands(rng, 48, 4096)
+    cq, csf = exact_operands(rng, 256, 4096)
+    d = lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(cq), i32_to_dev(csf), workspace=ws)
+    assert np.array_equal(to_np(d), mx.bf16_round(cr.gemm_nt(aq, asf, cq, csf)))
+
+
 def test_shared_workspace_across_shapes(lib):
     """One workspace reused by einsum and GEMM calls of different shapes keeps every result exact."""
     from mxfp8_activation_quantization_amd import binding as B
     rng = np.random.default_rng(91)
     shapes = [(129, 8, 4096, 1024, 5120), (64, 8, 4096, 1024, 5120), (200, 2, 2048, 256, 640)]
-    need = max(max(B.lib().grouped_fp8_einsum_workspace_size(M, G, K, N),
-                   B.lib().fp8_gemm_nt_workspace_size(M, P, G * N)) for M, G, K, N, P in shapes)
+    need = max(max(B.lib().grouped_fp8_einsum_workspace_size(B.MXFP8_ACT_MXFP8, M, G, K, N),
+                   B.lib().fp8_gemm_nt_workspace_size(B.MXFP8_ACT_MXFP8, M, P, G * N)) for M, G, K, N, P in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     for rep in range(2):
         for M, G, K, N, P in shapes:
