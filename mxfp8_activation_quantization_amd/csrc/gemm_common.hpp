@@ -269,7 +269,7 @@ __device__ __forceinline__ int xcd_work_index(int id, int total) {
   return (id % 8) * (total / 8) + id / 8;
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, int out, hipStream_t stream);
+hipError_t launch_gemm_tiled(const GemmArgs& p, const GemmPlan& plan, int64_t G, int out, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,
                               hipStream_t stream);
 

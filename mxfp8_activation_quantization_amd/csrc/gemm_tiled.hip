@@ -18,6 +18,7 @@
 // Token rows past M: the row part of every activation offset is in the per-lane
 // register, which the buffer range check covers (the scalar offset is not
 // checked), and the range ends at row M, so those rows arrive as zeros.
+#include <map>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -71,31 +72,21 @@ struct DlLds {
   static_assert(BYTES <= 160 * 1024, "LDS of one CU");
 };
 
+// One output tile: weight rows n0 .. n0 + BN - 1 of group g x tokens m0 .. m0 + BM - 1,
+// the whole K range.  `smem` is the workgroup's LDS (at least DlLds<C>::BYTES).
 template <class C, int OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
+__device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g, int64_t n0, int64_t m0) {
   static_assert(C::NW == 4, "four waves");
   constexpr int WI = C::BN / 64;                 // weight load instructions per wave and stage
   constexpr int XI = C::BM / 64;                 // activation load instructions per wave and stage
   constexpr int L = WI + XI;                     // loads per wave and stage
   constexpr int SI = (C::BN + C::BM) / 64;       // scale-word load instructions per wave and scale group
   using Lds = DlLds<C>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds::BYTES];
 
   // the wave index is uniform: keep it in a scalar register (load offsets and LDS bases derive from it)
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 5, i = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
-
-  const int total = G * m_tiles * n_tiles;
-  const int wi = xcd_work_index((int)blockIdx.x, total);
-  const int nt = wi % n_tiles;
-  const int rest = wi / n_tiles;
-  const int mt = rest % m_tiles;
-  const int g = rest / m_tiles;
-
-  const int64_t n0 = (int64_t)nt * C::BN;
-  const int64_t m0 = (int64_t)mt * C::BM;
   const int ksteps = (int)(p.K / 128);
   const int nst = 2 * ksteps;                    // half-step stages, 64 deep
   const int64_t rows_left = p.M - m0;
@@ -344,30 +335,52 @@ void dl_gemm_kernel(GemmArgs p, int G, int m_tiles, int n_tiles) {
 }
 
 // Tile configurations: 256 weight rows x 256 tokens; 128 x 256 when N is not a
-// multiple of 256.  The choice depends only on (G, N), never on the output mode.
+// multiple of 256 and for the last rows of tokens (below).
 using Cfg256 = BigCfg<256, 256, 2, 2>;   // 128 x 128 per wave
 using Cfg128 = BigCfg<128, 256, 1, 4>;   // 128 x 64 per wave
 
-template <class C, int OUT>
-static hipError_t launch_dl(const GemmArgs& p, int64_t G, hipStream_t stream) {
-  const int n_tiles = (int)(p.N / C::BN);
-  const int m_tiles = (int)((p.M + C::BM - 1) / C::BM);
-  const int64_t total = G * n_tiles * (int64_t)m_tiles;
-  hipLaunchKernelGGL((dl_gemm_kernel<C, OUT>), dim3((unsigned)total), dim3(256), 0, stream, p, (int)G, m_tiles,
-                     n_tiles);
+// The kernel: rows of 256 tokens [0, full_rows) as CF tiles, the remaining rows
+// as CT tiles (narrower: more of them, so a short last round of the machine is
+// spread over more CUs).  Each output element is one whole-K accumulation in
+// both, with the same operand bytes in the same order, so the tile shape never
+// changes a result.
+template <class CF, class CT, int OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void dl_gemm_kernel(GemmArgs p, int G, int full_rows, int rows) {
+  static_assert(CF::BM == 256 && CT::BM == 256, "rows of 256 tokens");
+  constexpr int BYTES = DlLds<CF>::BYTES > DlLds<CT>::BYTES ? DlLds<CF>::BYTES : DlLds<CT>::BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[BYTES];
+  const int nf = (int)(p.N / CF::BN), ntl = (int)(p.N / CT::BN);
+  const int F = G * nf * full_rows;
+  if ((int)blockIdx.x < F) {
+    const int wi = xcd_work_index((int)blockIdx.x, F);
+    const int nt = wi % nf, rest = wi / nf, mt = rest % full_rows, g = rest / full_rows;
+    dl_tile<CF, OUT>(p, smem, g, (int64_t)nt * CF::BN, (int64_t)mt * 256);
+  } else {
+    const int tr = rows - full_rows;
+    const int wi = xcd_work_index((int)blockIdx.x - F, G * ntl * tr);
+    const int nt = wi % ntl, rest = wi / ntl, mt = full_rows + rest % tr, g = rest / tr;
+    dl_tile<CT, OUT>(p, smem, g, (int64_t)nt * CT::BN, (int64_t)mt * 256);
+  }
+}
+
+template <class CF, class CT, int OUT>
+static hipError_t launch_dl(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
+  hipLaunchKernelGGL((dl_gemm_kernel<CF, CT, OUT>), dim3((unsigned)plan.workgroups), dim3(256), 0, stream, p, (int)G,
+                     plan.full_rows, plan.rows);
   return hipGetLastError();
 }
 
-template <class C>
-static hipError_t dispatch_out(const GemmArgs& p, int64_t G, int out, hipStream_t s) {
-  if (out == OUT_BF16) return launch_dl<C, OUT_BF16>(p, G, s);
-  if (out == OUT_MX) return launch_dl<C, OUT_MX>(p, G, s);
-  return launch_dl<C, OUT_BOTH>(p, G, s);
+template <class CF, class CT>
+static hipError_t dispatch_out(const GemmArgs& p, const GemmPlan& plan, int64_t G, int out, hipStream_t s) {
+  if (out == OUT_BF16) return launch_dl<CF, CT, OUT_BF16>(p, plan, G, s);
+  if (out == OUT_MX) return launch_dl<CF, CT, OUT_MX>(p, plan, G, s);
+  return launch_dl<CF, CT, OUT_BOTH>(p, plan, G, s);
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs& p, int64_t G, int out, hipStream_t stream) {
-  if (p.N % 256 == 0) return dispatch_out<Cfg256>(p, G, out, stream);
-  return dispatch_out<Cfg128>(p, G, out, stream);
+hipError_t launch_gemm_tiled(const GemmArgs& p, const GemmPlan& plan, int64_t G, int out, hipStream_t stream) {
+  if (p.N % 256 == 0) return dispatch_out<Cfg256, Cfg128>(p, plan, G, out, stream);
+  return dispatch_out<Cfg128, Cfg128>(p, plan, G, out, stream);
 }
 
 // Few-token plan (the streaming kernel)
@@ -379,6 +392,33 @@ constexpr int64_t kSkinnyMaxSteps = 32;       // 128-deep steps per split (the s
 // shape, so one shape's partial tiles never land on another shape's counters when
 // calls share a workspace.
 constexpr int64_t kCounterBytes = 65536;
+// Many-token tiles: one resident workgroup per CU on MI355X's 256 CUs; a
+// 128 x 256 tile takes about this fraction of a 256 x 256 tile's time.
+constexpr int64_t kTileCUs = 256;
+constexpr double kNarrowTileCost = 0.65;
+
+// Time until the last of n1 items of cost c1, then n2 items of cost c2, finishes
+// when they are dealt in order to `cus` identical workers, each item to the worker
+// free first.  Workers free at equal times are kept together, so this takes a
+// handful of steps per round however many items there are.
+static double dealt_makespan(int64_t n1, double c1, int64_t n2, double c2, int64_t cus) {
+  std::map<double, int64_t> free_at;
+  free_at[0.0] = cus;
+  auto deal = [&](int64_t n, double c) {
+    while (n > 0) {
+      auto it = free_at.begin();
+      const double t = it->first;
+      const int64_t k = it->second < n ? it->second : n;
+      it->second -= k;
+      if (it->second == 0) free_at.erase(it);
+      free_at[t + c] += k;
+      n -= k;
+    }
+  };
+  deal(n1, c1);
+  deal(n2, c2);
+  return free_at.rbegin()->first;
+}
 
 GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
   GemmPlan pl{};
@@ -387,8 +427,29 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
   const int64_t tiles = G * (N / 64) * chunks;
   pl.skinny = M <= kSkinnyMaxTokens && tiles * 8 <= kCounterBytes;     // one 64-bit counter per tile
   if (!pl.skinny) {
-    const int64_t bn = N % 256 == 0 ? 256 : 128;
-    pl.workgroups = G * (N / bn) * ((M + 255) / 256);
+    const int64_t rows = (M + 255) / 256;
+    pl.rows = (int)rows;
+    pl.full_rows = (int)rows;
+    if (N % 256 == 0) {
+      // How many rows of 256 tokens get 256-wide tiles: the one that finishes
+      // first when the tiles are dealt in order to kTileCUs CUs, one each, a
+      // 128-wide tile costing kNarrowTileCost of a 256-wide one (fewest narrow
+      // tiles among equal estimates).  Many rounds leave little to gain: skip.
+      const int64_t per_row = G * (N / 256);
+      if (per_row * rows < 4 * kTileCUs) {
+        double best = 1e30;
+        for (int64_t r = rows; r >= 0; --r) {
+          const double t = dealt_makespan(per_row * r, 1.0, 2 * per_row * (rows - r), kNarrowTileCost, kTileCUs);
+          if (t < best * 0.99) {
+            best = t;
+            pl.full_rows = (int)r;
+          }
+        }
+      }
+      pl.workgroups = per_row * pl.full_rows + 2 * per_row * (rows - pl.full_rows);
+    } else {
+      pl.workgroups = G * (N / 128) * rows;
+    }
     if (x_bf16 && M > 0) {
       // the tile kernel reads E4M3 activations: BF16 ones are quantized first, into the workspace
       // (after the counter region: a workspace shared with split-K calls keeps its counters)
@@ -422,7 +483,7 @@ hipError_t launch_gemm(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipSt
   const GemmPlan plan = plan_gemm(p.M, G, p.N, p.K, x_bf16);
   if (plan.skinny) return launch_gemm_skinny(p, plan, G, x_bf16, out, stream);
   if (x_bf16) return hipErrorInvalidValue;        // the caller quantizes into the workspace first
-  return launch_gemm_tiled(p, G, out, stream);
+  return launch_gemm_tiled(p, plan, G, out, stream);
 }
 
 }  // namespace mx

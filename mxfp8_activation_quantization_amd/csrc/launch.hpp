@@ -46,6 +46,8 @@ struct GemmPlan {
   int n_tiles;            // 64-row weight tiles per group (skinny)
   int splits;             // K splits (skinny)
   int64_t workgroups;
+  int full_rows;          // many tokens: rows of 256 tokens done as 256-wide weight tiles ...
+  int rows;               //   ... of all ceil(M / 256) rows; the rest as 128-wide tiles
   int64_t counter_bytes;  // leading part of the workspace: one 64-bit counter per (tile, chunk)
   int64_t stage_offset;   // BF16 activations, many tokens: codes [M][G*K] at this offset
   int64_t stage_sf_offset;//   and packed scales [M][G*K/128] at this one (0 when unused)
