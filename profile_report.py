@@ -12,10 +12,12 @@
         profiles/traffic_NAME.json (read by bench.py for roofline.traffic while
         the kernel sources are unchanged) and prints a Markdown summary.
 
-Kernels are told apart by name and output mode: the direct-to-LDS and
-streaming GEMM kernels carry their output mode as the last template argument
-(1 = BF16 out: fp8_gemm_nt, 2 = MXFP8 out: grouped_fp8_einsum); the quantize
-kernel is mxfp8_quantize.  Only the grid that occurs most often is kept for
+    python profile_report.py pmc P.csv [--title T] [--command C]
+        Mean of each collected counter per dispatch, for each launch of the chain.
+
+Kernels are told apart by name and output mode (the streaming kernel's second
+template argument, the tile kernel's last: 1 = BF16 out: fp8_gemm_nt, 2 = MXFP8
+out: grouped_fp8_einsum); the quantize kernel is mxfp8_quantize.  Only the grid that occurs most often is kept for
 each, which drops the one-off launches of the set-up (weight quantization).
 """
 from __future__ import annotations
@@ -37,14 +39,40 @@ def short_name(name: str) -> str:
     return s.replace("void mx::", "").replace("mx::", "").strip()
 
 
+def template_args(n: str):
+    """Top-level template arguments of `kernel<...>`, or None."""
+    i = n.find("<")
+    if i < 0 or not n.endswith(">"):
+        return None
+    args, depth, cur = [], 0, ""
+    for ch in n[i + 1:-1]:
+        if ch == "," and depth == 0:
+            args.append(cur.strip())
+            cur = ""
+            continue
+        depth += ch == "<"
+        depth -= ch == ">"
+        cur += ch
+    args.append(cur.strip())
+    return n[:i], args
+
+
 def chain_role(name: str):
+    """quantize / einsum (MXFP8 out) / gemm (BF16 out) from a kernel name: the output mode is the
+    second template argument of the streaming kernel and the last of the tile kernel."""
     n = short_name(name)
     if n.startswith("quantize_kernel"):
         return "quantize"
-    m = re.match(r"(dl_gemm_kernel|big_gemm_kernel|stream_kernel|splitk_kernel)<(.*)>$", n)
-    if not m:
+    t = template_args(n)
+    if not t:
         return None
-    out = m.group(2).split(",")[-1].strip()
+    kern, args = t
+    if kern == "stream_kernel" and len(args) >= 2:
+        out = args[1]
+    elif kern == "dl_gemm_kernel":
+        out = args[-1]
+    else:
+        return None
     return {"1": "gemm", "2": "einsum", "3": "einsum"}.get(out)
 
 
@@ -130,9 +158,38 @@ def cmd_traffic(a):
     print("\n".join(lines))
 
 
+def cmd_pmc(a):
+    """Mean of every counter per dispatch, per chain launch (most frequent grid)."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(a.csv) as f:
+        for r in csv.DictReader(f):
+            role = chain_role(r["Kernel_Name"])
+            if role:
+                vals[(role, int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if a.title:
+        print(f"# {a.title}\n")
+    if a.command:
+        print("Command (from the repository root, one MI355X):\n\n    " + a.command + "\n")
+    counters = sorted({c for v in vals.values() for c in v})
+    print("| launch | grid | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|---|" + "---|" * len(counters))
+    for role in ("quantize", "einsum", "gemm"):
+        keys = [k for k in vals if k[0] == role]
+        if not keys:
+            continue
+        k = max(keys, key=lambda k: len(next(iter(vals[k].values()))))
+        n = len(next(iter(vals[k].values())))
+        cells = [f"{sum(vals[k][c]) / len(vals[k][c]):.6g}" if vals[k].get(c) else "" for c in counters]
+        print(f"| {role} | {k[1]} | {n} | " + " | ".join(cells) + " |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    pm = sub.add_parser("pmc")
+    pm.add_argument("csv")
+    pm.add_argument("--title", default="")
+    pm.add_argument("--command", default="")
     k = sub.add_parser("kernels")
     k.add_argument("db")
     k.add_argument("--title", default="")
@@ -146,7 +203,7 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command", action="append")
     a = ap.parse_args()
-    {"kernels": cmd_kernels, "traffic": cmd_traffic}[a.cmd](a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "pmc": cmd_pmc}[a.cmd](a)
 
 
 if __name__ == "__main__":
