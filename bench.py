@@ -139,7 +139,8 @@ def time_arm_graphs(torch, graphs, stream, steps, warmup):
 
 
 def sweep(torch, L, Ms, dims, w, stream, args):
-    """Chain and x_fused µs/call over token counts, weights rotated as in the headline run."""
+    """µs/call of the chain, x_fused and unfused arms over token counts, weights rotated as in the headline
+    run; `fusion_saving_us` = unfused - chain (what the MXFP8 epilogue saves against a separate requantize)."""
     G, K, N, P = dims
     out = []
     gen = torch.Generator(device="cuda")
@@ -152,7 +153,7 @@ def sweep(torch, L, Ms, dims, w, stream, args):
                  "wa_q": w["wa_q"].clone(), "wa_sf": w["wa_sf"].clone(),
                  "wb_q": w["wb_q"].clone(), "wb_sf": w["wb_sf"].clone()} for r in range(R)]
         res = {"M": M}
-        for arm in ("chain", "x_fused"):
+        for arm in ("chain", "x_fused", "unfused"):
             # one graph with the chain once per rotating set, in a row (as consecutive layers)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.stream(stream):
@@ -173,10 +174,45 @@ def sweep(torch, L, Ms, dims, w, stream, args):
         res["tflops"] = flop / (us * 1e-6) / 1e12
         res["hbm_frac"] = sum(nb.values()) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
         res["mfma_frac"] = res["tflops"] / FP8_PEAK_TFLOPS
-        print(f"[bench] sweep M={M}: chain {us:.2f} us, x_fused {res['x_fused_us']:.2f} us, "
-              f"{res['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        res["fusion_saving_us"] = res["unfused_us"] - us
+        print(f"[bench] sweep M={M}: chain {us:.2f} us, x_fused {res['x_fused_us']:.2f} us, unfused "
+              f"{res['unfused_us']:.2f} us, {res['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         out.append(res)
         del sets, x
+        torch.cuda.empty_cache()
+    return out
+
+
+def quant_sweep(torch, L, si, stream, args):
+    """Standalone mxfp8_quantize over the quantize-sweep rows (BF16 [M, 7168] -> E4M3 + packed scales):
+    µs/launch from a graph of at least 16 launches over rotating inputs, and the HBM roofline fraction
+    of its 3.03125 bytes per element."""
+    out = []
+    K = si.QUANT_SWEEP_K
+    for M in si.QUANT_SWEEP_M:
+        x0 = torch.from_numpy(np.ascontiguousarray(si.quant_sweep_input(M)).view(np.int16)).view(
+            torch.bfloat16).to("cuda")
+        R = int(min(8, max(1, -(-ROTATE_BYTES // (x0.numel() * 3)))))
+        xs = [x0 if r == 0 else x0.clone() for r in range(R)]
+        qs = [torch.empty((M, K), dtype=torch.uint8, device="cuda") for _ in range(R)]
+        sfs = [torch.empty((M, K // 128), dtype=torch.int32, device="cuda") for _ in range(R)]
+        reps = max(1, -(-16 // R))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for r in range(R):
+                L.mxfp8_quantize(xs[r], q=qs[r], sf=sfs[r], stream=stream)
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(reps):
+                    for r in range(R):
+                        L.mxfp8_quantize(xs[r], q=qs[r], sf=sfs[r], stream=stream)
+        torch.cuda.synchronize()
+        n = max(2, min(args.steps, 200) // (reps * R))
+        us = time_arm_graphs(torch, [g], stream, n, 1) / (reps * R)
+        nbytes = M * K * (2 + 1) + M * (K // 32)
+        out.append({"M": M, "K": K, "us_per_launch": us, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
+        print(f"[bench] quantize sweep M={M}: {us:.2f} us/launch", file=sys.stderr, flush=True)
+        del g, xs, qs, sfs, x0
         torch.cuda.empty_cache()
     return out
 
@@ -192,6 +228,8 @@ def main():
     ap.add_argument("--sweep", default="",
                     help="comma-separated token counts: also time the chain and x_fused arms at each "
                          "(decode-config weights, x drawn on the device) and report them under 'sweep'")
+    ap.add_argument("--quant-sweep", action="store_true",
+                    help="also time the standalone quantizer on the quantize-sweep rows (M x 7168)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -386,6 +424,8 @@ def main():
     if args.sweep:
         line["sweep"] = sweep(torch, L, [int(v) for v in args.sweep.split(",") if v], (G, K, N, P),
                               sets[0], stream, args)
+    if args.quant_sweep:
+        line["quant_sweep"] = quant_sweep(torch, L, si, stream, args)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.config, inp)
