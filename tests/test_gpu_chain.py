@@ -68,6 +68,23 @@ def test_gemm_exact_regime_bitexact(lib, M, N, K):
     assert np.array_equal(to_np(d), ref)
 
 
+@pytest.mark.parametrize("kind,M,G,N,K", [("gemm", 4000, 1, 5120, 256), ("einsum", 2304, 8, 1024, 256)])
+def test_mixed_tile_shapes_bitexact(lib, kind, M, G, N, K):
+    """Launches whose last rows of tokens use the narrower tiles (wo_b at 4000 tokens: 12 of 16 rows of 256
+    tokens as 256-wide tiles; the einsum at 2304 tokens: 8 of 9): still bit-exact in the exact regime."""
+    rng = np.random.default_rng(4000 + M)
+    aq, asf = exact_operands(rng, M, G * K)
+    wq, wsf = exact_operands(rng, G * N, K)
+    if kind == "gemm":
+        d = lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq), i32_to_dev(wsf))
+        ref = mx.bf16_round(cr.gemm_nt(aq, asf, wq, wsf))
+    else:
+        d = lib.grouped_fp8_einsum(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq.reshape(G, N, K)),
+                                   i32_to_dev(wsf.reshape(G, N, K // 128)), out="bf16")
+        ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
+    assert np.array_equal(to_np(d), ref)
+
+
 @pytest.mark.parametrize("M,G,K,N", [(4, 2, 256, 128), (45, 3, 512, 256), (96, 8, 128, 128), (3, 2, 1152, 128),
                                      (64, 2, 4096, 256), (600, 2, 512, 512), (257, 3, 256, 128),
                                      (520, 2, 1024, 384)])
