@@ -34,9 +34,10 @@
  *     MXFP8_ERR_SHAPE.
  *   - Outputs must not overlap inputs or each other (MXFP8_ERR_ALIAS).
  *   - Workspace: the GEMM entry points may need device scratch -- split-K
- *     partial sums, and, for BF16 activations with more than 256 rows, the
- *     activations quantized to MXFP8 (the many-token kernel reads E4M3; the
- *     library quantizes BF16 input with mxfp8_quantize first).  The matching
+ *     partial sums, and, for BF16 activations that go to a kernel reading E4M3
+ *     (more than 256 rows, or at most 32 rows when each workgroup can take the
+ *     whole K range), the activations quantized to MXFP8 (the library quantizes
+ *     BF16 input with mxfp8_quantize first).  The matching
  *     *_workspace_size(kind, shape) call gives the bytes (0 = none needed,
  *     pointer may be NULL).  The caller owns it, zero-fills it once before first
  *     use (256-byte aligned).  Split-K calls keep arrival counters in its first
@@ -46,9 +47,10 @@
  *     share one.
  *   - Non-finite inputs are outside the contract (codes then unspecified).
  *   - Results are deterministic: the same inputs give the same bytes, and BF16
- *     and pre-quantized activations give identical results (few rows: the
- *     kernel quantizes BF16 in its load path with the quantizer's rule and the
- *     same split plan; many rows: the quantizer runs first).
+ *     and pre-quantized activations give identical results (the split-K
+ *     streaming kernel quantizes BF16 in its load path with the quantizer's
+ *     rule and the same split plan; before the other kernels the quantizer
+ *     runs first).
  */
 #ifndef MXFP8_H
 #define MXFP8_H

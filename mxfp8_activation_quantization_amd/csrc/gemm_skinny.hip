@@ -445,6 +445,201 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   if (tid == 0) __hip_atomic_store(cnt, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// ---------------------------------------------------------------------------
+// At most 64 tokens: whole K per workgroup, no split.
+//
+// With few tokens the activation bytes per weight row are small, so a workgroup
+// can own 32 weight rows over the whole K range and the grid still covers most of
+// the machine (wo_a: 256 workgroups, wo_b: 160); no partial tile leaves the
+// workgroup.  Up to 32 tokens (one token tile) the four waves take the 128-deep
+// steps in turn (step j: wave j % 4), each into its own accumulator; with 33 to 64
+// tokens (two token tiles) waves 2 tt and 2 tt + 1 take the even and odd steps of
+// token tile tt.  At the end the partial tiles of a token tile are added in wave
+// order through LDS and the first wave of the tile stores it.
+//
+// Ring: kGvStages stages of SS steps (SS = the waves per token tile, so every
+// wave multiplies one step of every stage); per step 32 weight rows and 8 XG token
+// rows x 128 bytes (XG = 1, 2, 4 or 8 groups of 8 token rows, the fewest that hold
+// M), the slot layout of the streaming kernel above.  The ring is shallow on
+// purpose: with every CU streaming at once, deeper rings (8 to 12 stages of two
+// steps were measured) finished later, and four stages of four steps (48 KB of
+// weights in flight per CU) were fastest at both wo_a and wo_b shapes.  Token
+// rows past M arrive as zeros or are not loaded at all; MFMA lanes of tokens past
+// the loaded rows read a loaded row again.  Those output columns are never
+// stored.  Scale tables for up to kGvMaxSteps steps are fetched once, at the start.
+constexpr int kGvMaxSteps = 64;
+constexpr int kGvStages = 4;
+
+template <int XG>
+struct GvCfg {
+  static constexpr int MT = XG > 4 ? 2 : 1;       // token tiles
+  static constexpr int SS = 4 / MT;               // steps per stage = waves per token tile
+  static constexpr int XR = 8 * XG;               // token rows in a stage
+  static constexpr int XI = XG > 4 ? 2 : 1;       // activation loads per wave and step, at most
+};
+
+template <int XG>
+struct GvStage {
+  uint8_t w[GvCfg<XG>::SS][32 * 128];
+  uint8_t x[GvCfg<XG>::SS][GvCfg<XG>::XR * 128];
+};
+
+// Scale table of rows x kGvMaxSteps words: word j of row r in 16-byte chunk
+// (j / 4) ^ (r % 16) of the row's 256 bytes (16 consecutive rows read one word
+// from 16 different chunk positions).
+__device__ __forceinline__ uint32_t gv_table_word(const uint32_t* tab, int r, int j) {
+  return tab[r * kGvMaxSteps + (((j >> 2) ^ (r & 15)) << 2) + (j & 3)];
+}
+
+// MFMA fragment of row r of a stage slot (chunks 4KS + q and 4KS + 2 + q).
+__device__ __forceinline__ v8i gv_frag(const uint8_t* op, int r, int KS, int q) {
+  const int g = g8(r);
+  const uint8_t* b = op + 128 * r;
+  return frag(*reinterpret_cast<const uint4*>(b + 16 * ((4 * KS + q) ^ g)),
+              *reinterpret_cast<const uint4*>(b + 16 * ((4 * KS + 2 + q) ^ g)));
+}
+
+// Waits until at most n stages (L loads each) of this wave's loads are in flight, n <= N.
+template <int L, int N>
+__device__ __forceinline__ void gv_wait(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) wait_vmcnt<N * L>();
+    else gv_wait<L, N - 1>(n);
+  }
+}
+
+template <int OUT, int XG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
+  using C = GvCfg<XG>;
+  constexpr int NS = kGvStages, SS = C::SS, XR = C::XR;
+  static_assert(NS >= 3 && SS * (1 + C::XI) * (NS - 2) <= 63, "ring depth within the vmcnt range");
+  __shared__ __attribute__((aligned(1024))) GvStage<XG> ring[NS];
+  __shared__ __attribute__((aligned(1024))) uint32_t wtab[32 * kGvMaxSteps];
+  __shared__ __attribute__((aligned(1024))) uint32_t xtab[XR * kGvMaxSteps];
+
+  const int total = G * n_tiles;
+  const int wi = xcd_work_index((int)blockIdx.x, total);
+  const int g = wi / n_tiles, nt = wi % n_tiles;
+  const int tid = threadIdx.x, lane = tid & 63, i = lane & 31, q = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tt = wave / SS, par = wave % SS;       // token tile, step parity
+
+  const int ksteps = (int)(p.K / 128);             // <= kGvMaxSteps (the plan guarantees it)
+  const int nst = (ksteps + SS - 1) / SS;
+  const int64_t n_row0 = (int64_t)g * p.N + (int64_t)nt * 32;
+  const int64_t m_rows = p.M < XR ? p.M : XR;     // the launch picks XG with M <= 8 XG
+  const int ldw = (int)p.K, ldx = (int)p.ld_x, ldxs = (int)(p.ld_xsf * 4);
+  const int xcol0 = (int)((int64_t)g * p.K), xsfcol0 = g * ksteps * 4;
+  const Rsrc rw = make_rsrc_sgpr(p.w + n_row0 * p.K, (int64_t)32 * p.K);
+  const Rsrc rws = make_rsrc_sgpr(p.w_sf + n_row0 * ksteps, (int64_t)32 * ksteps * 4);
+  // The row part of every activation offset is in the per-lane register (the part
+  // the range check covers): rows past M arrive as zeros and nothing past row M is read.
+  const Rsrc rx = make_rsrc_sgpr(p.x, m_rows * ldx);
+  const Rsrc rxs = make_rsrc_sgpr(p.x_sf, m_rows * ldxs);
+
+  // Load instruction n of an operand and step fills rows 8n .. 8n+7 (1 KB): the weights'
+  // instruction n = wave, the activations' n = wave + 4u (u < XI) while 8n < M.
+  const int lr = lane >> 3, lc = lane & 7;
+  const int vw = (8 * wave + lr) * ldw + (lc ^ g8(8 * wave + lr)) * 16;
+  int vx[C::XI];
+#pragma unroll
+  for (int u = 0; u < C::XI; ++u) {
+    const int r = 8 * (wave + 4 * u) + lr;
+    vx[u] = r * ldx + (lc ^ g8(r)) * 16;
+  }
+  const int nx = (8 * wave < m_rows ? 1 : 0) + (C::XI > 1 && 8 * (wave + 4) < m_rows ? 1 : 0);
+
+  // scale tables: instruction n covers rows 4n .. 4n+3; lane l loads chunk l % 16 of row
+  // 4n + l / 16 into position (l % 16) ^ (row % 16).  The whole offset is in the per-lane
+  // register (range-checked): a row's last chunks may read the next row's words (unused)
+  // or zeros past the end of the buffer.
+#pragma unroll
+  for (int n = wave; n < 8; n += 4) {
+    const int tr = 4 * n + (lane >> 4), ch = (lane & 15) ^ (tr & 15);
+    dl_load16(rws, wtab + n * 256, tr * ksteps * 4 + ch * 16, 0);
+  }
+#pragma unroll
+  for (int n = wave; n < XR / 4; n += 4) {
+    const int tr = 4 * n + (lane >> 4), ch = (lane & 15) ^ (tr & 15);
+    dl_load16(rxs, xtab + n * 256, tr * ldxs + xsfcol0 + ch * 16, 0);
+  }
+
+  // stage t: steps SS t .. SS t + SS - 1 (past the last step a stage loads the last step
+  // again: valid addresses, not multiplied)
+  auto issue = [&](int t) {
+    GvStage<XG>& st = ring[t % NS];
+#pragma unroll
+    for (int h = 0; h < SS; ++h) {
+      const int kk = SS * t + h, k = kk < ksteps ? kk : ksteps - 1;
+      dl_load16(rw, st.w[h] + wave * 1024, vw, k * 128);
+#pragma unroll
+      for (int u = 0; u < C::XI; ++u)
+        if (u < nx) dl_load16(rx, st.x[h] + (wave + 4 * u) * 1024, vx[u], xcol0 + k * 128);
+    }
+  };
+
+  const int xi = C::MT == 2 ? 32 * tt + i : (i & (XR - 1));   // the token row this lane reads
+  v16f acc = zero16();
+  auto loop = [&](auto l_tag) {
+    constexpr int L = decltype(l_tag)::value;       // this wave's loads per stage
+    const int pre = nst < NS - 1 ? nst : NS - 1;
+    for (int t = 0; t < pre; ++t) issue(t);
+    for (int t = 0; t < nst; ++t) {
+      const int later = nst - 1 - t;                // stages issued after t (at most NS - 2 in flight)
+      gv_wait<L, NS - 2>(later);
+      asm volatile("s_barrier" ::: "memory");     // stage t landed everywhere; stage t-1 is free
+      if (t + NS - 1 < nst) issue(t + NS - 1);
+      const GvStage<XG>& st = ring[t % NS];
+      const int j = SS * t + par;                   // this wave's step of the stage
+      if (j < ksteps) {
+        const int sw = (int)(gv_table_word(wtab, i, j) >> (8 * q));
+        const int sx = (int)(gv_table_word(xtab, xi, j) >> (8 * q));
+        acc = mfma_scaled<0>(gv_frag(st.w[par], i, 0, q), gv_frag(st.x[par], xi, 0, q), acc, sw, sx);
+        acc = mfma_scaled<2>(gv_frag(st.w[par], i, 1, q), gv_frag(st.x[par], xi, 1, q), acc, sw, sx);
+      }
+    }
+  };
+  if (nx == 0) loop(std::integral_constant<int, SS>{});
+  else if (C::XI == 1 || nx == 1) loop(std::integral_constant<int, 2 * SS>{});
+  else loop(std::integral_constant<int, 3 * SS>{});
+
+  // the partial tiles of each token tile, added in wave order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&ring[0]);  // 16 KB of the ring, no longer read
+  static_assert(sizeof(ring) >= 4 * 16 * 64 * 4, "reduction buffer fits the ring");
+  if (par > 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * 64 + lane] = acc[e];
+  }
+  __syncthreads();
+  if (par == 0) {
+    for (int w = 1; w < SS; ++w)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += red[((wave + w) * 16 + e) * 64 + lane];
+    const int64_t m = 32 * tt + i;
+    store_tile<OUT>(p, acc, m, m < p.M, n_row0, q);
+  }
+}
+
+template <int OUT, int XG>
+static hipError_t launch_whole_k_xg(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
+  hipLaunchKernelGGL((whole_k_kernel<OUT, XG>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p,
+                     (int)G, plan.n_tiles);
+  return hipGetLastError();
+}
+
+template <int OUT>
+static hipError_t launch_whole_k(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
+  if (p.M <= 8) return launch_whole_k_xg<OUT, 1>(p, plan, G, stream);
+  if (p.M <= 16) return launch_whole_k_xg<OUT, 2>(p, plan, G, stream);
+  if (p.M <= 32) return launch_whole_k_xg<OUT, 4>(p, plan, G, stream);
+  if (p.M <= 64) return launch_whole_k_xg<OUT, 8>(p, plan, G, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int MT, int OUT, bool XB>
 static hipError_t launch_stream(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
   hipLaunchKernelGGL((stream_kernel<MT, OUT, XB>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p, (int)G,
@@ -467,6 +662,12 @@ static hipError_t dispatch(const GemmArgs& p, const GemmPlan& plan, int64_t G, b
 
 hipError_t launch_gemm_skinny(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,
                               hipStream_t stream) {
+  if (plan.whole_k) {
+    if (x_bf16) return hipErrorInvalidValue;      // the caller quantizes into the workspace first
+    if (out == OUT_BF16) return launch_whole_k<OUT_BF16>(p, plan, G, stream);
+    if (out == OUT_MX) return launch_whole_k<OUT_MX>(p, plan, G, stream);
+    return launch_whole_k<OUT_BOTH>(p, plan, G, stream);
+  }
   if (plan.mt == 1) return dispatch<1>(p, plan, G, x_bf16, out, stream);
   return dispatch<2>(p, plan, G, x_bf16, out, stream);
 }

@@ -388,6 +388,18 @@ constexpr int64_t kSkinnyMaxTokens = 256;
 // The few-token kernels are sized for one resident round: one workgroup per CU.
 constexpr int64_t kSkinnyTargetWorkgroups = 256;
 constexpr int64_t kSkinnyMaxSteps = 32;       // 128-deep steps per split (the streaming kernel's scale tables)
+// Few tokens: a workgroup owns 32 weight rows over the whole K range (no split)
+// when K fits its scale tables and the grid is wide enough -- at least 128
+// workgroups up to 32 tokens, 256 (every CU) up to 64, where each workgroup also
+// takes in twice the activation bytes.  BF16 activations are quantized into the
+// workspace first.
+constexpr int64_t kWholeKMaxSteps = 64;
+
+static bool whole_k_fits(int64_t M, int64_t G, int64_t N, int64_t K) {
+  if (N % 32 != 0 || K / 128 > kWholeKMaxSteps) return false;
+  const int64_t workgroups = G * (N / 32);
+  return M <= 32 ? workgroups >= 128 : (M <= 64 && workgroups >= 256);
+}
 // The workspace always starts with this many bytes of arrival counters, whatever the
 // shape, so one shape's partial tiles never land on another shape's counters when
 // calls share a workspace.
@@ -420,6 +432,15 @@ static double dealt_makespan(int64_t n1, double c1, int64_t n2, double c2, int64
   return free_at.rbegin()->first;
 }
 
+// The tile and whole-K kernels read E4M3 activations: BF16 ones are quantized
+// first, into the workspace: codes [M][kt], then packed scales [M][kt/128] (after
+// the counter region, so a workspace shared with split-K calls keeps its counters).
+static void stage_bf16(GemmPlan& pl, int64_t M, int64_t kt) {
+  pl.stage_offset = kCounterBytes;
+  pl.stage_sf_offset = pl.stage_offset + (M * kt + 255) / 256 * 256;
+  pl.workspace_bytes = pl.stage_sf_offset + (M * (kt / 32) + 255) / 256 * 256;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
   GemmPlan pl{};
   const int mt = M <= 32 ? 1 : 2;
@@ -450,17 +471,20 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
     } else {
       pl.workgroups = G * (N / 128) * rows;
     }
-    if (x_bf16 && M > 0) {
-      // the tile kernel reads E4M3 activations: BF16 ones are quantized first, into the workspace
-      // (after the counter region: a workspace shared with split-K calls keeps its counters)
-      const int64_t kt = G * K;
-      pl.stage_offset = kCounterBytes;
-      pl.stage_sf_offset = pl.stage_offset + (M * kt + 255) / 256 * 256;
-      pl.workspace_bytes = pl.stage_sf_offset + (M * (kt / 32) + 255) / 256 * 256;
-    }
+    if (x_bf16 && M > 0) stage_bf16(pl, M, G * K);
     return pl;
   }
   const int64_t ksteps = K / 128;
+  if (whole_k_fits(M, G, N, K)) {
+    pl.whole_k = true;
+    pl.mt = M <= 32 ? 1 : 2;
+    pl.chunks = 1;
+    pl.n_tiles = (int)(N / 32);
+    pl.splits = 1;
+    pl.workgroups = G * (N / 32);
+    if (x_bf16 && M > 0) stage_bf16(pl, M, G * K);
+    return pl;
+  }
   int64_t splits = kSkinnyTargetWorkgroups / (tiles > 0 ? tiles : 1);
   const int64_t max_splits = ksteps / 4 > 1 ? ksteps / 4 : 1;     // at least two super-steps per split
   const int64_t min_splits = (ksteps + kSkinnyMaxSteps - 1) / kSkinnyMaxSteps;   // scale tables hold 32 steps

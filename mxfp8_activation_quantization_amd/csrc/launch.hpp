@@ -41,9 +41,10 @@ struct GemmArgs {
 // [M][G*K/128]).  `workspace_bytes` is 0 when nothing is needed.
 struct GemmPlan {
   bool skinny;
+  bool whole_k;           // skinny, at most 64 tokens: 32 weight rows x whole K per workgroup, no split
   int mt;                 // token tiles of 32 per workgroup (skinny)
   int chunks;             // token chunks (skinny)
-  int n_tiles;            // 64-row weight tiles per group (skinny)
+  int n_tiles;            // weight tiles per group (skinny: 64 rows; whole_k: 32 rows)
   int splits;             // K splits (skinny)
   int64_t workgroups;
   int full_rows;          // many tokens: rows of 256 tokens done as 256-wide weight tiles ...

@@ -153,17 +153,32 @@ def test_workspace_sizes():
     Q, BF = B.MXFP8_ACT_MXFP8, B.MXFP8_ACT_BF16
     # a K range shorter than two 256-deep super-steps per split is never split (no scratch); deeper K is
     # split across workgroups in the decode range only
-    assert LIB.grouped_fp8_einsum_workspace_size(Q, 64, 8, 512, 1024) == 0
-    need = LIB.grouped_fp8_einsum_workspace_size(Q, 64, 8, 4096, 1024)
+    assert LIB.grouped_fp8_einsum_workspace_size(Q, 64, 2, 512, 1024) == 0
+    need = LIB.grouped_fp8_einsum_workspace_size(Q, 64, 4, 4096, 1024)
     assert need > 0 and need % 256 == 0
-    assert LIB.grouped_fp8_einsum_workspace_size(BF, 64, 8, 4096, 1024) == need   # decode: quantized in the kernel
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 64, 4, 4096, 1024) == need   # split K: quantized in the kernel
     assert LIB.fp8_gemm_nt_workspace_size(Q, 64, 5120, 8192) > 0
+    # up to 64 tokens on a grid of 256 workgroups of 32 weight rows (wo_a): whole K per workgroup, no scratch;
+    # BF16 activations are quantized into the workspace first
+    assert LIB.grouped_fp8_einsum_workspace_size(Q, 64, 8, 4096, 1024) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 64, 8, 4096, 1024) == 65536 + 64 * 32768 + 64 * 1024
     assert LIB.fp8_gemm_nt_workspace_size(Q, 4096, 5120, 8192) == 0        # many tokens: no split
     # many BF16 tokens: the activations are quantized into the workspace first (codes + packed scales),
     # after the counter region that split-K calls sharing the workspace keep
     assert LIB.fp8_gemm_nt_workspace_size(BF, 4096, 5120, 8192) == 65536 + 4096 * 8192 + 4096 * 8192 // 32
     assert LIB.grouped_fp8_einsum_workspace_size(BF, 300, 8, 4096, 1024) >= 300 * 32768 * (1 + 1 / 32)
     assert LIB.fp8_gemm_nt_workspace_size(Q, 0, 5120, 8192) == 0
+    # at most 32 tokens on a wide enough weight: one workgroup per 32 weight rows and the whole K range,
+    # no split (E4M3: no scratch); BF16 activations are quantized into the workspace first
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 32, 5120, 8192) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(Q, 1, 8, 4096, 1024) == 0
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 33, 5120, 8192) > 0           # 160 workgroups: split K past 32
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 33, 8192, 8192) == 0
+    assert LIB.fp8_gemm_nt_workspace_size(BF, 1, 5120, 8192) == 65536 + 8192 + 256
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 7, 8, 4096, 1024) == 65536 + 7 * 32768 + 7 * 1024
+    # too narrow for the machine (64 workgroups) or K past the scale tables: split K as before
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 8, 2048, 8192) > 0
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 8, 5120, 8192 + 128) > 0
     assert LIB.grouped_fp8_einsum_workspace_size(Q, 64, 8, 4000, 1024) == -1
     assert LIB.fp8_gemm_nt_workspace_size(Q, 64, 100, 8192) == -1
     assert LIB.fp8_gemm_nt_workspace_size(7, 64, 128, 8192) == -1          # unknown activation kind

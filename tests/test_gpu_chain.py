@@ -85,6 +85,52 @@ def test_mixed_tile_shapes_bitexact(lib, kind, M, G, N, K):
     assert np.array_equal(to_np(d), ref)
 
 
+@pytest.mark.parametrize("M", [1, 7, 12, 32])
+@pytest.mark.parametrize("kind,G,N,K", [("gemm", 1, 4096, 8192), ("gemm", 1, 5120, 384), ("einsum", 8, 512, 256),
+                                        ("einsum", 4, 1024, 1152)])
+def test_whole_k_exact_regime_bitexact(lib, kind, M, G, N, K):
+    """At most 32 tokens with at least 128 workgroups of 32 weight rows: each workgroup takes the whole K
+    range (up to 64 steps of 128, odd step counts included) and its four waves' partial tiles are added at
+    the end; the ring holds 8, 16 or 32 token rows per step (M = 1, 7 | 12 | 32).  Bit-exact in the exact
+    regime, for every output form."""
+    rng = np.random.default_rng(7000 + M + K)
+    aq, asf = exact_operands(rng, M, G * K)
+    wq, wsf = exact_operands(rng, G * N, K)
+    if kind == "gemm":
+        d = lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq), i32_to_dev(wsf))
+        assert np.array_equal(to_np(d), mx.bf16_round(cr.gemm_nt(aq, asf, wq, wsf)))
+        return
+    ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq.reshape(G, N, K)),
+                                            i32_to_dev(wsf.reshape(G, N, K // 128)), out="both")
+    assert np.array_equal(to_np(z_b), ref)
+    oq, osf = mx.quantize(ref)
+    assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf)
+
+
+@pytest.mark.parametrize("M", [33, 40, 64])
+@pytest.mark.parametrize("kind,G,N,K", [("gemm", 1, 8192, 384), ("einsum", 8, 1024, 1152), ("einsum", 8, 1024, 8192)])
+def test_whole_k_two_token_tiles_bitexact(lib, kind, M, G, N, K):
+    """33 to 64 tokens on a grid of at least 256 workgroups: whole K per workgroup with two token tiles, each
+    summed by two waves (even and odd steps).  Bit-exact in the exact regime, every output form."""
+    from mxfp8_activation_quantization_amd import binding as B
+    rng = np.random.default_rng(8000 + M + K)
+    aq, asf = exact_operands(rng, M, G * K)
+    wq, wsf = exact_operands(rng, G * N, K)
+    if kind == "gemm":
+        assert B.lib().fp8_gemm_nt_workspace_size(B.MXFP8_ACT_MXFP8, M, N, K) == 0      # no split
+        d = lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq), i32_to_dev(wsf))
+        assert np.array_equal(to_np(d), mx.bf16_round(cr.gemm_nt(aq, asf, wq, wsf)))
+        return
+    assert B.lib().grouped_fp8_einsum_workspace_size(B.MXFP8_ACT_MXFP8, M, G, K, N) == 0
+    ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq.reshape(G, N, K)),
+                                            i32_to_dev(wsf.reshape(G, N, K // 128)), out="both")
+    assert np.array_equal(to_np(z_b), ref)
+    oq, osf = mx.quantize(ref)
+    assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf)
+
+
 @pytest.mark.parametrize("M,G,K,N", [(4, 2, 256, 128), (45, 3, 512, 256), (96, 8, 128, 128), (3, 2, 1152, 128),
                                      (64, 2, 4096, 256), (600, 2, 512, 512), (257, 3, 256, 128),
                                      (520, 2, 1024, 384)])
@@ -115,13 +161,14 @@ def _nan_padded(rows_valid, t, fill):
     return big[:rows_valid]
 
 
-@pytest.mark.parametrize("M", [7, 33, 290, 300])
-def test_rows_past_m_are_never_read(lib, M):
+@pytest.mark.parametrize("M,N,G,Ng", [(7, 512, 2, 256), (33, 512, 2, 256), (290, 512, 2, 256), (300, 512, 2, 256),
+                                     (7, 4096, 8, 512), (33, 8192, 8, 1024)])
+def test_rows_past_m_are_never_read(lib, M, N, G, Ng):
     """Exact regime (BF16 values that quantize exactly; sums exact in fp32) with activation storage that
     continues past row M with NaN bytes: every output must still equal the oracle bit for bit, for BF16
-    activations (quantized in the load path) and for E4M3 activations, in the GEMM and the einsum."""
-    rng = np.random.default_rng(300 + M)
-    N, K = 512, 1024
+    activations and for E4M3 activations, in the GEMM and the einsum (split-K, tile and whole-K kernels)."""
+    rng = np.random.default_rng(300 + M + N)
+    K = 1024
     a = rng.choice(EXACT_VALUES, size=(M, K))
     bq, bsf = exact_operands(rng, N, K)
     ref = mx.bf16_round(a.astype(np.float64) @ (mx.E4M3_TABLE[bq] * np.repeat(
@@ -132,8 +179,7 @@ def test_rows_past_m_are_never_read(lib, M):
     aq, asf = lib.mxfp8_quantize(at)
     aq_p, asf_p = _nan_padded(M, aq, 0x7F), _nan_padded(M, asf, -1)
     assert np.array_equal(to_np(lib.fp8_gemm_nt(aq_p, asf_p, b_t, bsf_t)), ref)
-    # einsum, two groups, BF16 and E4M3 x
-    G, Ng = 2, 256
+    # einsum, BF16 and E4M3 x
     x = rng.choice(EXACT_VALUES, size=(M, G * K))
     wq, wsf = exact_operands(rng, G * Ng, K)
     w_t, wsf_t = u8_to_dev(wq.reshape(G, Ng, K)), i32_to_dev(wsf.reshape(G, Ng, K // 128))
@@ -167,7 +213,7 @@ def test_split_k_workspace_counters_return_to_zero(lib):
 
 
 @pytest.mark.parametrize("kind,M,G,N,K", [("gemm", 48, 1, 256, 4096), ("gemm", 64, 1, 5120, 8192),
-                                          ("gemm", 5, 1, 128, 2176), ("einsum", 64, 8, 1024, 4096),
+                                          ("gemm", 5, 1, 128, 2176), ("einsum", 64, 4, 1024, 4096),
                                           ("einsum", 33, 3, 256, 1024)])
 def test_split_k_combine_modes_give_identical_bits(lib, kind, M, G, N, K):
     """The decode kernels combine split-K partials through one XCD's L2 (default), through memory, or by
@@ -299,11 +345,15 @@ def test_fused_z_equals_quantized_own_bf16(lib, name):
     assert torch.equal(z_q2, z_q) and torch.equal(z_sf2, z_sf) and torch.equal(z_b2, z_b)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "ragged"])
-def test_prequantized_x_equals_in_kernel_quantization(lib, name):
+@pytest.mark.parametrize("name,M", [("tiny", None), ("decode", None), ("ragged", None), ("ragged", 1),
+                                    ("ragged", 7), ("ragged", 32)])
+def test_prequantized_x_equals_in_kernel_quantization(lib, name, M):
+    """Holds on every kernel: the split-K streaming kernel quantizes BF16 in its load path; before the tile
+    kernel (many tokens) and the whole-K kernel (at most 32 tokens) the quantizer runs into the workspace."""
     c = get_case(name, lib)
-    xq, xsf = lib.mxfp8_quantize(c.x)
-    a = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
+    x = c.x if M is None else c.x[:M]
+    xq, xsf = lib.mxfp8_quantize(x)
+    a = lib.grouped_fp8_einsum(x, None, c.wa_q, c.wa_sf, out="both")
     b = lib.grouped_fp8_einsum(xq, xsf, c.wa_q, c.wa_sf, out="both")
     for u, v in zip(a, b):
         assert torch.equal(u, v)
@@ -362,9 +412,11 @@ def test_ragged_token_counts(lib, M):
     z_q, z_sf, z_b = lib.grouped_fp8_einsum(x, None, c.wa_q, c.wa_sf, out="both")
     check_z_against_oracle(z_q, z_sf, z_b, ref)
     check_out_against_oracle(c, out, z_q, z_sf, ref)
-    # rows are independent: the first M rows of the 300-row batch give the same bytes
+    # rows are independent: the first M rows of the 300-row batch agree with the M-row call to within the
+    # accumulation order (different token counts take different kernels: 300 rows the tile kernel, up to
+    # 32 the whole-K kernel, in between the split-K one)
     full = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="chain")
-    assert torch.equal(full[:M], out)
+    assert row_rel_err(to_np(out), mx.bf16_decode(to_np(full[:M])).astype(np.float64)).max() <= OUT_TOL
 
 
 def test_outputs_respect_strides_and_guards(lib):
