@@ -18,8 +18,16 @@
 namespace mx {
 
 constexpr int kQuantThreads = 256;
-constexpr int kSpansPerIter = 2;  // spans per 16-lane group per loop trip (loads in flight)
+constexpr int64_t kQuantMaxBlocks = 256 * 32;   // enough resident waves to cover HBM latency; the rest loops
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// SPI spans per 16-lane group and loop trip (loads in flight per lane).  Each
+// byte is read or written exactly once, so loads and stores are marked
+// non-temporal: measured on MI355X they stream 10-14% faster than plain ones
+// (BF16 [4096, 32768]: 73 -> 64 us).
+template <int SPI>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
     int32_t* __restrict__ sf, int64_t ld_sf, int64_t spans_per_row, int64_t total_spans) {
@@ -27,21 +35,21 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
   const int64_t groups = (int64_t)gridDim.x * (kQuantThreads / 16);
   int64_t g = (int64_t)blockIdx.x * (kQuantThreads / 16) + (threadIdx.x >> 4);
 
-  for (int64_t s0 = g * kSpansPerIter; s0 < total_spans; s0 += groups * kSpansPerIter) {
-    uint4 v[kSpansPerIter];
-    int64_t row[kSpansPerIter], w[kSpansPerIter];
+  for (int64_t s0 = g * SPI; s0 < total_spans; s0 += groups * SPI) {
+    uint4 v[SPI];
+    int64_t row[SPI], w[SPI];
 #pragma unroll
-    for (int u = 0; u < kSpansPerIter; ++u) {
+    for (int u = 0; u < SPI; ++u) {
       const int64_t s = s0 + u;
       row[u] = s / spans_per_row;
       w[u] = s - row[u] * spans_per_row;
+      v4u t = {0, 0, 0, 0};
       if (s < total_spans)
-        v[u] = *reinterpret_cast<const uint4*>(x + row[u] * ld_x + w[u] * 128 + j * 8);
-      else
-        v[u] = make_uint4(0, 0, 0, 0);
+        t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + row[u] * ld_x + w[u] * 128 + j * 8));
+      v[u] = make_uint4(t.x, t.y, t.z, t.w);
     }
 #pragma unroll
-    for (int u = 0; u < kSpansPerIter; ++u) {
+    for (int u = 0; u < SPI; ++u) {
       uint32_t m = amax_pair(amax_pair(amax_pair(amax_pair(0u, v[u].x), v[u].y), v[u].z), v[u].w);
       m = fold_pair(m);
       m = max(m, (uint32_t)__shfl_xor((int)m, 1, 16));
@@ -55,7 +63,8 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
       const uint32_t s2 = (uint32_t)__shfl((int)sb, 8, 16);
       const uint32_t s3 = (uint32_t)__shfl((int)sb, 12, 16);
       if (s0 + u < total_spans) {
-        *reinterpret_cast<uint2*>(q + row[u] * ld_q + w[u] * 128 + j * 8) = make_uint2(c0, c1);
+        const v2u cv = {c0, c1};
+        __builtin_nontemporal_store(cv, reinterpret_cast<v2u*>(q + row[u] * ld_q + w[u] * 128 + j * 8));
         if (j == 0) sf[row[u] * ld_sf + w[u]] = (int32_t)(sb | (s1 << 8) | (s2 << 16) | (s3 << 24));
       }
     }
@@ -66,15 +75,21 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, vo
                            int32_t* sf, int64_t ld_sf, hipStream_t stream) {
   const int64_t spans_per_row = K / 128;
   const int64_t total = M * spans_per_row;
-  const int64_t groups_needed = (total + kSpansPerIter - 1) / kSpansPerIter;
   const int64_t per_block = kQuantThreads / 16;
-  int64_t blocks = (groups_needed + per_block - 1) / per_block;
-  const int64_t cap = 256 * 32;  // enough resident waves to cover HBM latency; the rest loops
-  if (blocks > cap) blocks = cap;
+  // two spans per trip while that fills the grid; four once the grid is at its cap
+  const int64_t blocks2 = (total + 2 * per_block - 1) / (2 * per_block);
+  const bool wide = blocks2 > kQuantMaxBlocks;
+  int64_t blocks = wide ? (total + 4 * per_block - 1) / (4 * per_block) : blocks2;
+  if (blocks > kQuantMaxBlocks) blocks = kQuantMaxBlocks;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), ld_x, static_cast<uint8_t*>(q), ld_q, sf, ld_sf,
-                     spans_per_row, total);
+  auto* xp = static_cast<const uint16_t*>(x);
+  auto* qp = static_cast<uint8_t*>(q);
+  if (wide)
+    hipLaunchKernelGGL(quantize_kernel<4>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, xp, ld_x, qp, ld_q,
+                       sf, ld_sf, spans_per_row, total);
+  else
+    hipLaunchKernelGGL(quantize_kernel<2>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, xp, ld_x, qp, ld_q,
+                       sf, ld_sf, spans_per_row, total);
   return hipGetLastError();
 }
 

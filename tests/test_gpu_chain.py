@@ -207,8 +207,7 @@ def test_split_k_workspace_counters_return_to_zero(lib):
             for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(o, outs[0]) for o in outs)
-    tiles = (N // 64) * 1
-    assert int(ws[:8 * tiles].view(torch.int32).abs().sum()) == 0      # one 64-bit counter per tile
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0           # the whole counter region
     assert np.array_equal(to_np(outs[0]), mx.bf16_round(cr.gemm_nt(aq, asf, bq, bsf)))
 
 
@@ -251,6 +250,65 @@ def test_split_k_combine_modes_give_identical_bits(lib, kind, M, G, N, K):
     else:
         ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
     assert np.array_equal(outs["local"], ref)
+
+
+def _modes_bitexact(lib, kind, M, G, N, K, seed, modes=("local", "through", "recompute", "local")):
+    """Runs one exact-regime call per combine mode on one workspace; every output form must equal the oracle
+    bit for bit and the counter region must be zero again after each call."""
+    from mxfp8_activation_quantization_amd import binding as B
+    rng = np.random.default_rng(seed)
+    aq, asf = exact_operands(rng, M, G * K)
+    wq, wsf = exact_operands(rng, G * N, K)
+    a_t, asf_t = u8_to_dev(aq), i32_to_dev(asf)
+    need = (B.lib().fp8_gemm_nt_workspace_size(B.MXFP8_ACT_MXFP8, M, N, K) if kind == "gemm"
+            else B.lib().grouped_fp8_einsum_workspace_size(B.MXFP8_ACT_MXFP8, M, G, K, N))
+    ws = torch.zeros(max(need, 65536), dtype=torch.uint8, device=dev())
+    if kind == "gemm":
+        ref = mx.bf16_round(cr.gemm_nt(aq, asf, wq, wsf))
+        w_t, wsf_t = u8_to_dev(wq), i32_to_dev(wsf)
+    else:
+        ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
+        oq, osf = mx.quantize(ref)
+        w_t, wsf_t = u8_to_dev(wq.reshape(G, N, K)), i32_to_dev(wsf.reshape(G, N, K // 128))
+    try:
+        for mode in modes:
+            lib.set_splitk_mode(mode)
+            if kind == "gemm":
+                d = lib.fp8_gemm_nt(a_t, asf_t, w_t, wsf_t, workspace=ws)
+                assert np.array_equal(to_np(d), ref), mode
+            else:
+                z_q, z_sf, z_b = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="both", workspace=ws)
+                assert np.array_equal(to_np(z_b), ref), mode
+                assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf), mode
+                z_q2, z_sf2 = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="mxfp8", workspace=ws)
+                assert torch.equal(z_q2, z_q) and torch.equal(z_sf2, z_sf), mode
+                z_b2 = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="bf16", workspace=ws)
+                assert torch.equal(z_b2, z_b), mode
+            torch.cuda.synchronize()
+            assert int(ws[:65536].view(torch.int32).abs().sum()) == 0, mode
+    finally:
+        lib.set_splitk_mode("local")
+
+
+@pytest.mark.parametrize("M", [1, 20, 33, 64])
+@pytest.mark.parametrize("kind,G,N,K", [("einsum", 8, 1024, 4096), ("gemm", 1, 5120, 8192)])
+def test_decode_shapes_bitexact(lib, kind, M, G, N, K):
+    """The decode shapes (wo_a 8 x 4096 -> 1024 and wo_b 8192 -> 5120) at up to 64 tokens, whichever decode
+    kernel takes them: in the exact regime every output form equals the oracle bit for bit in each combine
+    mode, and the counter region of the workspace is zero again after every call."""
+    _modes_bitexact(lib, kind, M, G, N, K, 9100 + M + N)
+
+
+@pytest.mark.parametrize("kind,M,G,N,K", [("gemm", 65, 1, 5120, 8192), ("gemm", 300, 1, 5120, 2048),
+                                          ("gemm", 512, 1, 2560, 4096), ("gemm", 300, 1, 384, 1024),
+                                          ("einsum", 129, 8, 1024, 4096), ("einsum", 256, 4, 1024, 2048),
+                                          ("einsum", 700, 2, 1024, 1024), ("einsum", 97, 3, 384, 1152)])
+def test_mid_range_shapes_bitexact(lib, kind, M, G, N, K):
+    """65 to about 1000 tokens (split-K streaming kernel up to 256 tokens, tiles of 256 tokens above; 256- and
+    128-wide weight tiles, ragged token counts, K ranges that are not multiples of four steps): bit-exact
+    against the oracle in the exact regime in each combine mode, for every output form; counters return to
+    zero."""
+    _modes_bitexact(lib, kind, M, G, N, K, 9300 + M + N)
 
 
 # --------------------------------------------------------------------------- configs
