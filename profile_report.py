@@ -16,8 +16,9 @@
         Mean of each collected counter per dispatch, for each launch of the chain.
 
 Kernels are told apart by name and output mode (the streaming kernel's second
-template argument, the tile kernel's last: 1 = BF16 out: fp8_gemm_nt, 2 = MXFP8
-out: grouped_fp8_einsum); the quantize kernel is mxfp8_quantize.  Only the grid that occurs most often is kept for
+template argument, the whole-K kernel's first, the tile kernel's last: 1 = BF16
+out: fp8_gemm_nt, 2 = MXFP8 out: grouped_fp8_einsum); the quantize kernel is
+mxfp8_quantize.  Only the grid that occurs most often is kept for
 each, which drops the one-off launches of the set-up (weight quantization).
 """
 from __future__ import annotations
@@ -69,6 +70,8 @@ def chain_role(name: str):
     kern, args = t
     if kern == "stream_kernel" and len(args) >= 2:
         out = args[1]
+    elif kern == "whole_k_kernel":
+        out = args[0]
     elif kern == "dl_gemm_kernel":
         out = args[-1]
     else:
