@@ -217,6 +217,62 @@ def quant_sweep(torch, L, si, stream, args):
     return out
 
 
+def producer_sweep(torch, L, si, stream, args):
+    """The RMS-normalizing MXFP8 producer (mxfp8_rmsnorm_quantize) over the quantize-sweep rows
+    (BF16 [M, 7168]), with and without its BF16 output, next to the unfused pair it replaces (the producer
+    writing BF16 y only, then a standalone mxfp8_quantize of y) and the standalone quantize alone.  µs/launch from graphs of >= 16 launches over rotating
+    inputs; HBM roofline fraction of the algorithmic bytes (x read once, codes + scales written, the BF16 y
+    when written; gamma is 14 KB, read from cache)."""
+    out = []
+    K = si.QUANT_SWEEP_K
+    g = torch.from_numpy(si.rmsnorm_gamma(K).view(np.int16)).view(torch.bfloat16).to("cuda")
+    for M in si.QUANT_SWEEP_M:
+        x0 = torch.from_numpy(np.ascontiguousarray(si.quant_sweep_input(M)).view(np.int16)).view(
+            torch.bfloat16).to("cuda")
+        R = int(min(8, max(1, -(-ROTATE_BYTES // (x0.numel() * 5)))))
+        xs = [x0 if r == 0 else x0.clone() for r in range(R)]
+        ys = [torch.empty((M, K), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        qs = [torch.empty((M, K), dtype=torch.uint8, device="cuda") for _ in range(R)]
+        sfs = [torch.empty((M, K // 128), dtype=torch.int32, device="cuda") for _ in range(R)]
+        reps = max(1, -(-16 // R))
+        arms = {
+            "fused": lambda r: L.mxfp8_rmsnorm_quantize(xs[r], g, 1e-6, q=qs[r], sf=sfs[r], stream=stream),
+            "fused_bf16_out": lambda r: L.mxfp8_rmsnorm_quantize(xs[r], g, 1e-6, y=ys[r], q=qs[r], sf=sfs[r],
+                                                                  stream=stream),
+            "quantize_only": lambda r: L.mxfp8_quantize(xs[r], q=qs[r], sf=sfs[r], stream=stream),
+            # the arrangement the fusion replaces: the producer writes BF16 y, a standalone quantize reads it
+            "unfused": lambda r: (L.mxfp8_rmsnorm_quantize(xs[r], g, 1e-6, mxfp8_out=False, y=ys[r], stream=stream),
+                                  L.mxfp8_quantize(ys[r], q=qs[r], sf=sfs[r], stream=stream)),
+        }
+        res = {"M": M, "K": K}
+        for name, fn in arms.items():
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                for r in range(R):
+                    fn(r)
+                stream.synchronize()
+                with torch.cuda.graph(gr, stream=stream):
+                    for _ in range(reps):
+                        for r in range(R):
+                            fn(r)
+            torch.cuda.synchronize()
+            n = max(2, min(args.steps, 200) // (reps * R))
+            us = time_arm_graphs(torch, [gr], stream, n, 1) / (reps * R)
+            nbytes = M * K * 2 + M * K + M * (K // 32) + (M * K * 2 if name == "fused_bf16_out" else 0) + (
+                M * K * 4 if name == "unfused" else 0)                 # unfused: BF16 y written and read back
+            res[f"{name}_us"] = us
+            res[f"{name}_hbm_frac"] = nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+            del gr
+        res["fusion_saving_us"] = res["unfused_us"] - res["fused_bf16_out_us"]
+        print(f"[bench] producer sweep M={M}: fused {res['fused_us']:.2f} us, with BF16 out "
+              f"{res['fused_bf16_out_us']:.2f} us, unfused {res['unfused_us']:.2f} us, quantize alone "
+              f"{res['quantize_only_us']:.2f} us", file=sys.stderr, flush=True)
+        out.append(res)
+        del xs, ys, qs, sfs, x0
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +286,9 @@ def main():
                          "(decode-config weights, x drawn on the device) and report them under 'sweep'")
     ap.add_argument("--quant-sweep", action="store_true",
                     help="also time the standalone quantizer on the quantize-sweep rows (M x 7168)")
+    ap.add_argument("--producer-sweep", action="store_true",
+                    help="also time the RMS-normalizing MXFP8 producer on the quantize-sweep rows (M x 7168), "
+                         "next to the standalone quantizer it replaces")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -426,6 +485,8 @@ def main():
                               sets[0], stream, args)
     if args.quant_sweep:
         line["quant_sweep"] = quant_sweep(torch, L, si, stream, args)
+    if args.producer_sweep:
+        line["producer_sweep"] = producer_sweep(torch, L, si, stream, args)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.config, inp)

@@ -125,6 +125,34 @@ int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x,
                    void* q, int64_t ld_q, int32_t* sf, int64_t ld_sf, void* stream);
 
 /*
+ * mxfp8_rmsnorm_quantize -- RMS normalization of BF16 rows whose output leaves
+ * as MXFP8 (and optionally BF16): the producer-side fusion of vLLM PR #57977
+ * (before/after diagrams, Pieces), where the normalizing producer in front of
+ * the fused wqa/wkv projection emits that GEMM's MXFP8 input (codes + packed
+ * UE8M0 scales) itself instead of a standalone quantize launch.
+ *
+ *   x      BF16 [M][ld_x], row length K                (input)
+ *   gamma  BF16 [K], the per-column weight              (input)
+ *   eps    positive, finite                             (added to the mean square)
+ *   y      BF16 [M][ld_y], row length K, or NULL        (output, optional)
+ *   q      E4M3 [M][ld_q] bytes, row length K, or NULL  (output)
+ *   sf     int32 [M][ld_sf], K/128 words per row, or NULL (output, packed UE8M0 scales)
+ *
+ * Per row: y = BF16_RNE((x * r) * gamma) with r = 1 / sqrt(sum(x^2) / K + eps),
+ * all in fp32 (the sum of squares in a fixed order); (q, sf) = mxfp8_quantize of
+ * that BF16 y, bit for bit.  q and sf come together (both or neither); at least
+ * one of y and (q, sf) must be given (MXFP8_ERR_UNSUPPORTED otherwise) -- y
+ * alone is the unfused producer, whose output a standalone mxfp8_quantize then
+ * reads.  K must be a positive multiple of 128; ld_x, ld_q, ld_y >= K,
+ * ld_sf >= K/128; row strides 16-byte aligned.  Errors: as mxfp8_quantize, plus
+ * MXFP8_ERR_SHAPE for eps <= 0 or not finite and MXFP8_ERR_ALIAS when an output
+ * overlaps x, gamma or another output.
+ */
+int mxfp8_rmsnorm_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, const void* gamma, float eps,
+                           void* y, int64_t ld_y, void* q, int64_t ld_q, int32_t* sf, int64_t ld_sf,
+                           void* stream);
+
+/*
  * grouped_fp8_einsum -- the wo_a projection: G independent groups
  *     z[m, g*N + n] = sum_k x[m, g*K + k] * w[g, n, k]
  * with MXFP8 operands and fp32 accumulation (vLLM PR #60118, Validation:

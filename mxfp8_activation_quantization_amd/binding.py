@@ -41,6 +41,8 @@ SIGNATURES = {
     "mxfp8_device_check": (c_int, []),
     "mxfp8_set_splitk_mode": (c_int, [c_int]),
     "mxfp8_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "mxfp8_rmsnorm_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, c_vp, c_i64, c_vp, c_i64,
+                                       c_vp, c_i64, c_vp]),
     "grouped_fp8_einsum": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
                                    c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "grouped_fp8_einsum_workspace_size": (c_i64, [c_int, c_i64, c_i64, c_i64, c_i64]),
@@ -158,6 +160,38 @@ def mxfp8_quantize(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Ten
     _check(_lib.mxfp8_quantize(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(sf), sf.stride(0),
                                _stream(stream)), "mxfp8_quantize")
     return q, sf
+
+
+def mxfp8_rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, *, bf16_out: bool = False,
+                           mxfp8_out: bool = True, y: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                           sf: torch.Tensor | None = None, stream=None):
+    """RMSNorm of BF16 rows, leaving as MXFP8: (q uint8 [M, K], sf int32 [M, K/128]); (y, q, sf) with the BF16
+    y when bf16_out (or y) is given; y alone with mxfp8_out=False.  gamma: BF16 [K]."""
+    _rows(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if gamma.dtype != torch.bfloat16 or gamma.dim() != 1 or gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous BF16 vector of the row length")
+    if y is None and (bf16_out or not mxfp8_out):
+        y = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    if y is not None:
+        _rows(y, torch.bfloat16, "y")
+    if mxfp8_out:
+        if q is None:
+            q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        if sf is None:
+            sf = torch.empty((M, max(K // 128, 1)), dtype=torch.int32, device=x.device)
+        _rows(q, torch.uint8, "q")
+        _rows(sf, torch.int32, "sf")
+    else:
+        q = sf = None
+    _check(_lib.mxfp8_rmsnorm_quantize(_ptr(x), M, K, x.stride(0), _ptr(gamma), float(eps), _ptr(y),
+                                       y.stride(0) if y is not None else 0, _ptr(q),
+                                       q.stride(0) if q is not None else 0, _ptr(sf),
+                                       sf.stride(0) if sf is not None else 0, _stream(stream)),
+           "mxfp8_rmsnorm_quantize")
+    if not mxfp8_out:
+        return y
+    return (y, q, sf) if y is not None else (q, sf)
 
 
 def quantize_weight(w: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:

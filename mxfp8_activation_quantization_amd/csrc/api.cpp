@@ -159,6 +159,35 @@ MX_API int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, voi
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
+MX_API int mxfp8_rmsnorm_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, const void* gamma, float eps,
+                                  void* y, int64_t ld_y, void* q, int64_t ld_q, int32_t* sf, int64_t ld_sf,
+                                  void* stream) {
+  if (M < 0 || K <= 0 || K % 128) return MXFP8_ERR_SHAPE;
+  if (M > INT32_MAX) return MXFP8_ERR_SHAPE;
+  if (!(eps > 0.0f) || !(eps < 3.4e38f)) return MXFP8_ERR_SHAPE;   // positive and finite (NaN fails too)
+  const bool want_mx = q != nullptr || sf != nullptr;
+  if (!want_mx && !y) return MXFP8_ERR_UNSUPPORTED;                 // no output requested
+  if (want_mx && (ld_q < K || ld_sf < K / 128)) return MXFP8_ERR_SHAPE;
+  if (ld_x < K || (y && ld_y < K)) return MXFP8_ERR_SHAPE;
+  if ((ld_x * 2) % 16 || (want_mx && ld_q % 16) || (y && (ld_y * 2) % 16)) return MXFP8_ERR_ALIGN;
+  if (M == 0) return MXFP8_OK;
+  if (!x || !gamma || (want_mx && (!q || !sf))) return MXFP8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || (want_mx && (!aligned(q, 16) || !aligned(sf, 4))) ||
+      (y && !aligned(y, 16)))
+    return MXFP8_ERR_ALIGN;
+  const Range rx = range2d(x, M, K, ld_x, 2), rg = range2d(gamma, 1, K, K, 2),
+              rq = want_mx ? range2d(q, M, K, ld_q, 1) : Range{},
+              rs = want_mx ? range2d(sf, M, K / 128, ld_sf, 4) : Range{}, ry = y ? range2d(y, M, K, ld_y, 2) : Range{};
+  const Range outs[3] = {rq, rs, ry};
+  for (const Range& o : outs)
+    if (overlaps(o, rx) || overlaps(o, rg)) return MXFP8_ERR_ALIAS;
+  if (overlaps(rq, rs) || overlaps(rq, ry) || overlaps(rs, ry)) return MXFP8_ERR_ALIAS;
+  if (const int d = device_check(); d != MXFP8_OK) return d;
+  const hipError_t e = mx::launch_rmsnorm_quantize(x, M, K, ld_x, gamma, eps, y, ld_y, q, ld_q, sf, ld_sf,
+                                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
 MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf,
                               int64_t M, int64_t G, int64_t K, int64_t N, const void* w, const int32_t* w_sf,
                               void* z_q, int64_t ld_z, int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb,

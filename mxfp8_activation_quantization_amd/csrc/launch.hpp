@@ -60,6 +60,11 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16);
 hipError_t launch_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, void* q, int64_t ld_q,
                            int32_t* sf, int64_t ld_sf, hipStream_t stream);
 
+// RMS normalization of BF16 rows, BF16 output (optional) and MXFP8 output.
+hipError_t launch_rmsnorm_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, const void* gamma, float eps,
+                                   void* y, int64_t ld_y, void* q, int64_t ld_q, int32_t* sf, int64_t ld_sf,
+                                   hipStream_t stream);
+
 // out: 1 = BF16 only, 2 = MXFP8 only, 3 = both.  p.ws_* must point into a
 // workspace of at least plan_gemm(...).workspace_bytes when that is non-zero.
 hipError_t launch_gemm(const GemmArgs& p, int64_t G, bool x_bf16, int out, hipStream_t stream);

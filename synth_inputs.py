@@ -27,7 +27,8 @@ Recipe (all draws float32, then one RNE rounding to BF16):
     test (GPU) or the oracle's quantizer (CPU), never here.
   * Quantize sweep rows ~ N(0, 1); for M >= 7, n = max(1, round(0.01 M)) rows
     are scaled by 1e3 and n other rows are all zero (rows drawn without
-    replacement).
+    replacement).  The same rows feed the RMS-normalizing producer, whose
+    weight gamma ~ N(1, 0.1) in BF16.
 """
 from __future__ import annotations
 
@@ -139,6 +140,16 @@ def chain_inputs(shape: ChainShape, seed: int, outlier_rate: float = 0.0,
 def config_inputs(name: str, with_weights: bool = True) -> dict:
     cfg = CHAIN_CONFIGS[name]
     return chain_inputs(cfg.shape, cfg.seed, cfg.outlier_rate, with_weights)
+
+
+RMSNORM_GAMMA_SEED = SEED_BASE + 6
+
+
+def rmsnorm_gamma(K: int = QUANT_SWEEP_K, seed: int = RMSNORM_GAMMA_SEED) -> np.ndarray:
+    """BF16 bits [K] of an RMS-normalization weight: N(1, 0.1) (the weight is not on the pages; a weight
+    near one with a spread of ten percent stands in for a trained one)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed))).standard_normal(K, dtype=np.float32)
+    return bf16_bits((np.float32(1.0) + np.float32(0.1) * g).reshape(1, K))[0]
 
 
 def quant_sweep_input(M: int, K: int = QUANT_SWEEP_K, seed: int = QUANT_SWEEP_SEED) -> np.ndarray:

@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_chain_entry_points():
     names = declared_functions()
     for n in ("mxfp8_quantize", "grouped_fp8_einsum", "fp8_gemm_nt", "mxfp8_status_string",
-              "mxfp8_device_check", "mxfp8_version"):
+              "mxfp8_device_check", "mxfp8_version", "mxfp8_rmsnorm_quantize"):
         assert n in names
 
 
@@ -77,6 +77,39 @@ def test_quantize_argument_errors():
     assert quant(q=X + 512) == B.MXFP8_ERR_ALIAS          # codes written into the input
     assert quant(sf=Q + 64) == B.MXFP8_ERR_ALIAS
     assert quant(M=0, x=None, q=None, sf=None) == B.MXFP8_OK   # empty batch is a no-op
+
+
+def rms(M=4, K=256, ld_x=None, gamma=W, eps=1e-6, y=None, ld_y=0, q=Q, ld_q=None, sf=SF, ld_sf=None, x=X):
+    return LIB.mxfp8_rmsnorm_quantize(x, M, K, ld_x or K, gamma, eps, y, ld_y, q, ld_q or K, sf, ld_sf or K // 128,
+                                      None)
+
+
+def test_rmsnorm_quantize_argument_errors():
+    assert rms(M=-1) == B.MXFP8_ERR_SHAPE
+    assert rms(K=96) == B.MXFP8_ERR_SHAPE
+    assert rms(eps=0.0) == B.MXFP8_ERR_SHAPE                # eps must be positive
+    assert rms(eps=-1e-6) == B.MXFP8_ERR_SHAPE
+    assert rms(eps=float("nan")) == B.MXFP8_ERR_SHAPE
+    assert rms(eps=float("inf")) == B.MXFP8_ERR_SHAPE
+    assert rms(ld_x=200) == B.MXFP8_ERR_SHAPE
+    assert rms(y=ZB, ld_y=100) == B.MXFP8_ERR_SHAPE
+    assert rms(ld_x=260) == B.MXFP8_ERR_ALIGN
+    assert rms(gamma=None) == B.MXFP8_ERR_NULL
+    assert rms(sf=None) == B.MXFP8_ERR_NULL
+    assert rms(gamma=W + 8) == B.MXFP8_ERR_ALIGN
+    assert rms(y=ZB + 8, ld_y=256) == B.MXFP8_ERR_ALIGN
+    assert rms(q=X + 256) == B.MXFP8_ERR_ALIAS             # codes written into the input
+    assert rms(q=W) == B.MXFP8_ERR_ALIAS                   # codes written into gamma
+    assert rms(y=Q + 64, ld_y=256) == B.MXFP8_ERR_ALIAS    # BF16 output over the codes
+    assert rms(q=None, sf=None) == B.MXFP8_ERR_UNSUPPORTED    # no output at all
+    assert rms(q=None) == B.MXFP8_ERR_NULL                     # codes and scales come together
+    assert rms(M=0, x=None, gamma=None, q=None, sf=None, y=ZB, ld_y=256) == B.MXFP8_OK
+
+
+@pytest.mark.skipif(HAVE_GPU, reason="a GPU is present")
+def test_valid_rmsnorm_quantize_reports_missing_device():
+    assert rms() == B.MXFP8_ERR_DEVICE
+    assert rms(y=ZB, ld_y=256) == B.MXFP8_ERR_DEVICE
 
 
 WS = 0x10000000 * 12
