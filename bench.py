@@ -12,13 +12,19 @@ layers of a model do.
 
 Printed: one JSON line.  `value` is chain TFLOP/s at the configuration's token
 count; `ms_per_step` its time per call.  Besides the headline arm ("chain") it
-reports the arm whose einsum quantizes BF16 x in its load path ("x_fused", two
-launches) and the unfused arm ("unfused": BF16 z re-quantized by a separate
+reports the arm that hands the einsum BF16 x ("x_fused": the library quantizes it
+in the load path of the split-K decode kernel, otherwise into the workspace
+first) and the unfused arm ("unfused": BF16 z re-quantized by a separate
 launch, the arrangement the fused epilogue replaces), per-kernel durations from
 HIP events on the launch stream, the dominant kernel's roofline fraction, and the
 CPU oracle timed on this host's cores.  Per-kernel durations come from graphs of
 one kernel each, replayed back to back, so they compare with a profiler's kernel
-trace of the same command.
+trace of the same command.  By default the line also carries the chain over 20
+token counts from 1 to 32768 ("sweep"), the standalone quantizer on the
+quantize-sweep rows ("quant_sweep") and the RMS-normalizing producer on the same
+rows ("producer_sweep"); --sweep '' --no-quant-sweep --no-producer-sweep leaves
+them out (profiling runs do, so that their kernel traces hold the configuration's
+launches only).
 """
 from __future__ import annotations
 
@@ -38,6 +44,8 @@ METRIC = "o_proj chain µs/call + TFLOP/s (% HBM/FP8-MFMA roofline) at M=1..3276
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 ROTATE_BYTES = 600 << 20
+# token counts of the chain sweep: decode (1-256), 384, and prefill (512-32768)
+DEFAULT_SWEEP = "1,2,4,8,16,32,64,128,192,256,384,512,768,1024,2048,4096,8192,16384,24576,32768"
 KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_skinny.hip", "gemm_common.hpp", "quantize.hip", "mx_device.hpp"]
 KERNEL_NAMES = {"quantize": "mxfp8_quantize", "einsum": "grouped_fp8_einsum", "gemm": "fp8_gemm_nt"}
 
@@ -281,12 +289,13 @@ def main():
     ap.add_argument("--config", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--arms", default="chain,x_fused,unfused")
-    ap.add_argument("--sweep", default="",
-                    help="comma-separated token counts: also time the chain and x_fused arms at each "
-                         "(decode-config weights, x drawn on the device) and report them under 'sweep'")
-    ap.add_argument("--quant-sweep", action="store_true",
+    ap.add_argument("--sweep", default=DEFAULT_SWEEP,
+                    help="comma-separated token counts: also time the chain, x_fused and unfused arms at each "
+                         "(decode-config weights, x drawn on the device) and report them under 'sweep' "
+                         "('' for none)")
+    ap.add_argument("--quant-sweep", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the standalone quantizer on the quantize-sweep rows (M x 7168)")
-    ap.add_argument("--producer-sweep", action="store_true",
+    ap.add_argument("--producer-sweep", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the RMS-normalizing MXFP8 producer on the quantize-sweep rows (M x 7168), "
                          "next to the standalone quantizer it replaces")
     ap.add_argument("--copy-mib", type=int, default=0,
