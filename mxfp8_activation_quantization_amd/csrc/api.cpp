@@ -98,13 +98,14 @@ int bind_workspace(const mx::GemmPlan& plan, void* ws, int64_t ws_bytes, mx::Gem
   return MXFP8_OK;
 }
 
-// Launches the GEMM of p.  BF16 activations that the plan routes to the tile or
-// whole-K kernel are first quantized with the standalone quantizer into the workspace
+// Launches the GEMM of p.  BF16 activations that the plan routes to the tile kernel
+// (or to the whole-K kernel beyond its in-kernel quantization) are first quantized
+// with the standalone quantizer into the workspace
 // (codes [M][kt], scales [M][kt/128]); the tile kernel then reads those, so the
 // result is the one pre-quantized activations give.
 hipError_t launch(mx::GemmArgs p, const mx::GemmPlan& plan, int64_t G, bool x_bf16, int out, void* ws,
                   hipStream_t stream) {
-  if (x_bf16 && (!plan.skinny || plan.whole_k)) {
+  if (x_bf16 && (!plan.skinny || (plan.whole_k && !plan.whole_k_bf16))) {
     const int64_t kt = G * p.K;
     uint8_t* q = static_cast<uint8_t*>(ws) + plan.stage_offset;
     int32_t* sf = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + plan.stage_sf_offset);

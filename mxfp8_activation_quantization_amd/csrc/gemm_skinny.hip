@@ -335,6 +335,13 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
         if (t + 1 < nst) step(B, t + 1, false);
       }
       wait_vmcnt<0>();                               // the switched-off loads of the last steps
+      // Those loads still write A and B when they return: the registers stay
+      // allocated (tied here) until the wait above, so nothing else lives in them.
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        tie_after_wait(A.v[u]);
+        tie_after_wait(B.v[u]);
+      }
       return acc;
     }
 
@@ -624,6 +631,198 @@ void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
   }
 }
 
+// BF16 activations, at most 16 tokens, K of 32 or 64 steps: the whole-K kernel with
+// the activations quantized in its load path instead of by a separate launch.
+// Each thread owns BPT 32-element blocks of a stage's activation slot (step h,
+// token row r, block b), loads their BF16 bytes into registers two stages ahead,
+// and quantizes them by the quantizer's rule into the slot (codes) and the scale
+// table (scale bytes) -- the same bytes the standalone quantizer writes, so the
+// result is the one pre-quantized activations give.  The stage count is a
+// compile-time constant: every register set, load and wait below is static.
+template <int OUT, int XG, int NST>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
+  using C = GvCfg<XG>;
+  static_assert(XG <= 2, "at most 16 tokens");
+  constexpr int NS = kGvStages, SS = C::SS, XR = C::XR;
+  constexpr int KSTEPS = SS * NST;
+  static_assert(KSTEPS <= kGvMaxSteps, "scale tables hold kGvMaxSteps steps");
+  constexpr int BLK = SS * XR * 4;                 // activation blocks per stage
+  constexpr int BPT = BLK >= kThreads ? BLK / kThreads : 1;
+  static_assert((BLK % kThreads == 0 || BLK < kThreads) && BLK % 64 == 0, "whole blocks per thread and wave");
+  __shared__ __attribute__((aligned(1024))) GvStage<XG> ring[NS];
+  __shared__ __attribute__((aligned(1024))) uint32_t wtab[32 * kGvMaxSteps];
+  __shared__ __attribute__((aligned(1024))) uint32_t xtab[XR * kGvMaxSteps];
+
+  const int total = G * n_tiles;
+  const int wi = xcd_work_index((int)blockIdx.x, total);
+  const int g = wi / n_tiles, nt = wi % n_tiles;
+  const int tid = threadIdx.x, lane = tid & 63, i = lane & 31, q = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int par = wave % SS;                       // this wave's step of each stage
+
+  const int64_t n_row0 = (int64_t)g * p.N + (int64_t)nt * 32;
+  const int64_t m_rows = p.M < XR ? p.M : XR;
+  const int ldw = KSTEPS * 128, ldx2 = (int)p.ld_x * 2;
+  const int xcol0b = g * KSTEPS * 256;             // first BF16 byte of the group's columns
+  const Rsrc rw = make_rsrc_sgpr(p.w + n_row0 * ldw, (int64_t)32 * ldw);
+  const Rsrc rws = make_rsrc_sgpr(p.w_sf + n_row0 * KSTEPS, (int64_t)32 * KSTEPS * 4);
+  // BF16 rows: the row part of the offset is in the per-lane register, so rows past M read as zeros
+  const Rsrc rx = make_rsrc_sgpr(p.x, m_rows * ldx2);
+  const Rsrc rnull = make_rsrc_sgpr(p.w, 0);
+  const int lr = lane >> 3, lc = lane & 7;
+  const int vw = (8 * wave + lr) * ldw + (lc ^ g8(8 * wave + lr)) * 16;
+
+#pragma unroll
+  for (int n = wave; n < 8; n += 4) {
+    const int tr = 4 * n + (lane >> 4), ch = (lane & 15) ^ (tr & 15);
+    dl_load16(rws, wtab + n * 256, tr * KSTEPS * 4 + ch * 16, 0);
+  }
+
+  // this thread's blocks: index tid + kThreads u -> step h, token row r, block b of the stage
+  int bh[BPT], br[BPT], bb[BPT], vxo[BPT];
+  bool has[BPT];
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) {
+    const int bi = tid + kThreads * u;
+    has[u] = 64 * wave + kThreads * u < BLK;        // BLK is a multiple of 64: uniform per wave
+    bh[u] = (bi / (XR * 4)) % SS;
+    br[u] = (bi % (XR * 4)) / 4;
+    bb[u] = bi % 4;
+    // per-lane part (range-checked): row, then step and block within the stage's 4 x 256 bytes
+    // of the row -- at most 1 KB past the row start, less than a row stride (ld_x >= 4096)
+    vxo[u] = br[u] * ldx2 + bh[u] * 256 + bb[u] * 64;
+  }
+  struct XRegs { v4i v[4 * BPT]; };
+  auto load_x = [&](XRegs& X, int t) {
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const bool on = has[u] && t < NST;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        X.v[4 * u + c] = buf_load16(on ? rx : rnull, vxo[u] + 16 * c, xcol0b + SS * t * 256);
+    }
+  };
+  auto quantize_x = [&](XRegs& X, int t) {
+    GvStage<XG>& st = ring[t % NS];
+    uint8_t* xt = reinterpret_cast<uint8_t*>(xtab);
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      if (!has[u]) continue;
+      uint32_t w[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        w[4 * c] = (uint32_t)X.v[4 * u + c].x;
+        w[4 * c + 1] = (uint32_t)X.v[4 * u + c].y;
+        w[4 * c + 2] = (uint32_t)X.v[4 * u + c].z;
+        w[4 * c + 3] = (uint32_t)X.v[4 * u + c].w;
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) am = amax_pair(am, w[k]);
+      const int e = scale_exp_from_amax(fold_pair(am));
+      const float sc = exp2_int(e);
+      uint32_t cd[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cd[k] = encode4(w[2 * k], w[2 * k + 1], sc);
+      const int r = br[u], b = bb[u], gr = g8(r);
+      uint8_t* slot = st.x[bh[u]];
+      *reinterpret_cast<uint4*>(slot + 16 * (8 * r + ((2 * b) ^ gr))) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
+      *reinterpret_cast<uint4*>(slot + 16 * (8 * r + ((2 * b + 1) ^ gr))) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
+      const int j = SS * t + bh[u];
+      xt[4 * (r * kGvMaxSteps + (((j >> 2) ^ (r & 15)) << 2) + (j & 3)) + b] = (uint8_t)(e + 127);
+    }
+  };
+  // weights of stage t (one 1 KB load per wave and step), switched off past the last stage
+  auto issue_w = [&](int t) {
+    GvStage<XG>& st = ring[t % NS];
+    const bool on = t < NST;
+#pragma unroll
+    for (int h = 0; h < SS; ++h) dl_load16(on ? rw : rnull, st.w[h] + wave * 1024, vw, (SS * t + h) * 128);
+  };
+
+  const int xi = i & (XR - 1);                     // the token row this lane reads
+  v16f acc = zero16();
+  XRegs A, B;
+  load_x(A, 0);
+  load_x(B, 1);
+  issue_w(0);
+  issue_w(1);
+  issue_w(2);
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int u = 0; u < 4 * BPT; ++u) {
+    tie_after_wait(A.v[u]);
+    tie_after_wait(B.v[u]);
+  }
+  quantize_x(A, 0);
+  quantize_x(B, 1);
+  load_x(A, 2);
+  load_x(B, 3);
+  // iteration t: the registers of stage t+2 (set t % 2) are complete once only the
+  // previous iteration's batch (SS weight loads, and 4 BPT activation loads while
+  // stage t+3 exists) is in flight.  Activation loads past the last stage are not
+  // issued at all: a load whose registers the compiler takes as dead would still
+  // write them when it returns.
+  static_for<NST>([&](auto t_tag) {
+    constexpr int t = decltype(t_tag)::value;
+    XRegs& X = (t % 2 == 0) ? A : B;
+    if constexpr (t == 0) wait_vmcnt<4 * BPT>();
+    else wait_vmcnt<SS + (t + 3 < NST ? 4 * BPT : 0)>();
+#pragma unroll
+    for (int u = 0; u < 4 * BPT; ++u) tie_after_wait(X.v[u]);
+    lds_barrier();                                  // stage t landed and quantized everywhere; t-1 is free
+    if constexpr (t + 2 < NST) quantize_x(X, t + 2);
+    issue_w(t + 3);
+    if constexpr (t + 4 < NST) load_x(X, t + 4);
+    const GvStage<XG>& st = ring[t % NS];
+    const int j = SS * t + par;
+    const int sw = (int)(gv_table_word(wtab, i, j) >> (8 * q));
+    const int sx = (int)(gv_table_word(xtab, xi, j) >> (8 * q));
+    acc = mfma_scaled<0>(gv_frag(st.w[par], i, 0, q), gv_frag(st.x[par], xi, 0, q), acc, sw, sx);
+    acc = mfma_scaled<2>(gv_frag(st.w[par], i, 1, q), gv_frag(st.x[par], xi, 1, q), acc, sw, sx);
+  });
+  wait_vmcnt<0>();                                  // the switched-off weight loads of the last iterations
+
+  // the partial tiles of the four waves, added in wave order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&ring[0]);
+  static_assert(sizeof(ring) >= 4 * 16 * 64 * 4, "reduction buffer fits the ring");
+  if (par > 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * 64 + lane] = acc[e];
+  }
+  __syncthreads();
+  if (par == 0) {
+    for (int w = 1; w < SS; ++w)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += red[((wave + w) * 16 + e) * 64 + lane];
+    const int64_t m = i;
+    store_tile<OUT>(p, acc, m, m < p.M, n_row0, q);
+  }
+}
+
+template <int OUT, int XG>
+static hipError_t launch_whole_k_xb(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
+  const dim3 grid((unsigned)plan.workgroups), block(kThreads);
+  if (p.K == 32 * 128)
+    hipLaunchKernelGGL((whole_k_xb_kernel<OUT, XG, 32 / GvCfg<XG>::SS>), grid, block, 0, stream, p, (int)G,
+                       plan.n_tiles);
+  else if (p.K == 64 * 128)
+    hipLaunchKernelGGL((whole_k_xb_kernel<OUT, XG, 64 / GvCfg<XG>::SS>), grid, block, 0, stream, p, (int)G,
+                       plan.n_tiles);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int OUT>
+static hipError_t launch_whole_k_bf16(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
+  if (p.M <= 8) return launch_whole_k_xb<OUT, 1>(p, plan, G, stream);
+  if (p.M <= 16) return launch_whole_k_xb<OUT, 2>(p, plan, G, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int OUT, int XG>
 static hipError_t launch_whole_k_xg(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
   hipLaunchKernelGGL((whole_k_kernel<OUT, XG>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p,
@@ -663,7 +862,12 @@ static hipError_t dispatch(const GemmArgs& p, const GemmPlan& plan, int64_t G, b
 hipError_t launch_gemm_skinny(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,
                               hipStream_t stream) {
   if (plan.whole_k) {
-    if (x_bf16) return hipErrorInvalidValue;      // the caller quantizes into the workspace first
+    if (x_bf16) {
+      if (!plan.whole_k_bf16) return hipErrorInvalidValue;   // the caller quantizes into the workspace first
+      if (out == OUT_BF16) return launch_whole_k_bf16<OUT_BF16>(p, plan, G, stream);
+      if (out == OUT_MX) return launch_whole_k_bf16<OUT_MX>(p, plan, G, stream);
+      return launch_whole_k_bf16<OUT_BOTH>(p, plan, G, stream);
+    }
     if (out == OUT_BF16) return launch_whole_k<OUT_BF16>(p, plan, G, stream);
     if (out == OUT_MX) return launch_whole_k<OUT_MX>(p, plan, G, stream);
     return launch_whole_k<OUT_BOTH>(p, plan, G, stream);

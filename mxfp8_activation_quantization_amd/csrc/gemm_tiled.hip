@@ -482,7 +482,12 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
     pl.n_tiles = (int)(N / 32);
     pl.splits = 1;
     pl.workgroups = G * (N / 32);
-    if (x_bf16 && M > 0) stage_bf16(pl, M, G * K);
+    // BF16 activations: quantized in the load path up to 16 tokens with K of 32 or 64
+    // steps (the decode shapes); otherwise by the standalone quantizer into the workspace.
+    // Measured (wo_a, 8 x 4096 -> 1024): in the load path 9.2 / 9.4 / 10.7 / 14.7 us at
+    // 1 / 8 / 16 / 32 tokens against quantize + kernel 10.6 / 11.0 / 11.4 / 12.0.
+    pl.whole_k_bf16 = x_bf16 && M <= 16 && (ksteps == 32 || ksteps == 64);
+    if (x_bf16 && M > 0 && !pl.whole_k_bf16) stage_bf16(pl, M, G * K);
     return pl;
   }
   int64_t splits = kSkinnyTargetWorkgroups / (tiles > 0 ? tiles : 1);

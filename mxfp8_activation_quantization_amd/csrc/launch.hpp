@@ -42,6 +42,7 @@ struct GemmArgs {
 struct GemmPlan {
   bool skinny;
   bool whole_k;           // skinny, at most 64 tokens: 32 weight rows x whole K per workgroup, no split
+  bool whole_k_bf16;      // whole_k with BF16 activations quantized in the kernel's load path
   int mt;                 // token tiles of 32 per workgroup (skinny)
   int chunks;             // token chunks (skinny)
   int n_tiles;            // weight tiles per group (skinny: 64 rows; whole_k: 32 rows)

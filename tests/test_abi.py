@@ -207,8 +207,12 @@ def test_workspace_sizes():
     assert LIB.grouped_fp8_einsum_workspace_size(Q, 1, 8, 4096, 1024) == 0
     assert LIB.fp8_gemm_nt_workspace_size(Q, 33, 5120, 8192) > 0           # 160 workgroups: split K past 32
     assert LIB.fp8_gemm_nt_workspace_size(Q, 33, 8192, 8192) == 0
-    assert LIB.fp8_gemm_nt_workspace_size(BF, 1, 5120, 8192) == 65536 + 8192 + 256
-    assert LIB.grouped_fp8_einsum_workspace_size(BF, 7, 8, 4096, 1024) == 65536 + 7 * 32768 + 7 * 1024
+    # ... except up to 16 tokens with K of 32 or 64 steps (the decode shapes): quantized in the load path
+    assert LIB.fp8_gemm_nt_workspace_size(BF, 1, 5120, 8192) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 7, 8, 4096, 1024) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 16, 8, 4096, 1024) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(BF, 17, 8, 4096, 1024) == 65536 + 17 * 32768 + 17 * 1024
+    assert LIB.fp8_gemm_nt_workspace_size(BF, 16, 4096, 6144) == 65536 + 16 * 6144 + 16 * 6144 // 32   # 48 steps
     # too narrow for the machine (64 workgroups) or K past the scale tables: split K as before
     assert LIB.fp8_gemm_nt_workspace_size(Q, 8, 2048, 8192) > 0
     assert LIB.fp8_gemm_nt_workspace_size(Q, 8, 5120, 8192 + 128) > 0

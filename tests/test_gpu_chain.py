@@ -406,8 +406,9 @@ def test_fused_z_equals_quantized_own_bf16(lib, name):
 @pytest.mark.parametrize("name,M", [("tiny", None), ("decode", None), ("ragged", None), ("ragged", 1),
                                     ("ragged", 7), ("ragged", 32)])
 def test_prequantized_x_equals_in_kernel_quantization(lib, name, M):
-    """Holds on every kernel: the split-K streaming kernel quantizes BF16 in its load path; before the tile
-    kernel (many tokens) and the whole-K kernel (at most 32 tokens) the quantizer runs into the workspace."""
+    """Holds on every kernel: the split-K streaming kernel and (up to 32 tokens at the decode depths) the
+    whole-K kernel quantize BF16 in their load path; before the tile kernel (many tokens) and the whole-K
+    kernel at other depths the quantizer runs into the workspace."""
     c = get_case(name, lib)
     x = c.x if M is None else c.x[:M]
     xq, xsf = lib.mxfp8_quantize(x)
@@ -419,6 +420,36 @@ def test_prequantized_x_equals_in_kernel_quantization(lib, name, M):
     z_b = a[2]
     zq, zsf = lib.mxfp8_quantize(z_b)
     assert torch.equal(lib.fp8_gemm_nt(z_b, None, c.wb_q, c.wb_sf), lib.fp8_gemm_nt(zq, zsf, c.wb_q, c.wb_sf))
+
+
+@pytest.mark.parametrize("M", [1, 5, 8, 9, 16, 17, 31, 32])
+@pytest.mark.parametrize("kind,G,N,K", [("einsum", 8, 1024, 4096), ("gemm", 1, 5120, 8192), ("einsum", 4, 1024, 8192)])
+def test_whole_k_bf16_activations_equal_prequantized(lib, kind, M, G, N, K):
+    """Up to 16 tokens on the decode depths (K of 32 or 64 steps) the whole-K kernel quantizes BF16
+    activations in its load path (no workspace, no separate launch); from 17 to 32 the quantizer runs into
+    the workspace first.  Either way every output is bit-identical to the same call on pre-quantized
+    activations, for every row-group size and ragged token count; BF16 storage past row M is NaN and never
+    read."""
+    from mxfp8_activation_quantization_amd import binding as B
+    rng = np.random.default_rng(9500 + M + K)
+    xf = rng.standard_normal((M, G * K)).astype(np.float32)
+    xf[rng.random(xf.shape) < 1e-3] *= 100.0
+    x = _nan_padded(M, torch.from_numpy(xf).to(torch.bfloat16).to(dev()), 0x7FC0)
+    wq, wsf = exact_operands(rng, G * N, K)
+    xq, xsf = lib.mxfp8_quantize(x)
+    if kind == "gemm":
+        assert (B.lib().fp8_gemm_nt_workspace_size(B.MXFP8_ACT_BF16, M, N, K) == 0) == (M <= 16)
+        w_t, wsf_t = u8_to_dev(wq), i32_to_dev(wsf)
+        assert torch.equal(lib.fp8_gemm_nt(x, None, w_t, wsf_t), lib.fp8_gemm_nt(xq, xsf, w_t, wsf_t))
+        return
+    assert (B.lib().grouped_fp8_einsum_workspace_size(B.MXFP8_ACT_BF16, M, G, K, N) == 0) == (M <= 16)
+    w_t, wsf_t = u8_to_dev(wq.reshape(G, N, K)), i32_to_dev(wsf.reshape(G, N, K // 128))
+    a = lib.grouped_fp8_einsum(x, None, w_t, wsf_t, out="both")
+    b = lib.grouped_fp8_einsum(xq, xsf, w_t, wsf_t, out="both")
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    zq, zsf = lib.grouped_fp8_einsum(x, None, w_t, wsf_t, out="mxfp8")
+    assert torch.equal(zq, a[0]) and torch.equal(zsf, a[1])
 
 
 def check_out_against_oracle(c, out, z_q, z_sf, ref):
