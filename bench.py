@@ -22,7 +22,7 @@ one kernel each, replayed back to back, so they compare with a profiler's kernel
 trace of the same command.  By default the line also carries the chain over 20
 token counts from 1 to 32768 ("sweep"), the standalone quantizer on the
 quantize-sweep rows ("quant_sweep") and the RMS-normalizing producer on the same
-rows ("producer_sweep"); --sweep '' --no-quant-sweep --no-producer-sweep leaves
+rows ("producer_sweep"); --no-sweep --no-quant-sweep --no-producer-sweep leaves
 them out (profiling runs do, so that their kernel traces hold the configuration's
 launches only).
 """
@@ -293,6 +293,8 @@ def main():
                     help="comma-separated token counts: also time the chain, x_fused and unfused arms at each "
                          "(decode-config weights, x drawn on the device) and report them under 'sweep' "
                          "('' for none)")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_const", const="",
+                    help="leave the chain sweep out (same as --sweep '')")
     ap.add_argument("--quant-sweep", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the standalone quantizer on the quantize-sweep rows (M x 7168)")
     ap.add_argument("--producer-sweep", action=argparse.BooleanOptionalAction, default=True,

@@ -60,7 +60,8 @@ def template_args(n: str):
 
 def chain_role(name: str):
     """quantize / einsum (MXFP8 out) / gemm (BF16 out) from a kernel name: the output mode is the
-    second template argument of the streaming kernel and the last of the tile kernel."""
+    second template argument of the streaming kernel, the first of the whole-K kernels and the last
+    of the tile kernel."""
     n = short_name(name)
     if n.startswith("quantize_kernel"):
         return "quantize"
@@ -70,7 +71,7 @@ def chain_role(name: str):
     kern, args = t
     if kern == "stream_kernel" and len(args) >= 2:
         out = args[1]
-    elif kern == "whole_k_kernel":
+    elif kern in ("whole_k_kernel", "whole_k_xb_kernel"):
         out = args[0]
     elif kern == "dl_gemm_kernel":
         out = args[-1]
