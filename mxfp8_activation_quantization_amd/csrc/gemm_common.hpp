@@ -202,6 +202,40 @@ __device__ __forceinline__ void dl_load4(const Rsrc& r, const void* lds, int vof
                :: "s"(lds_addr(lds)), "v"(voff), "s"(r.v), "s"(soff) : "memory");
 }
 
+// Indexed forms of the LDS-DMA loads for unrolled load sequences: per-lane offset
+// voff + I * vstep (+ vadd), LDS destination lds_base + LDSOFF, with every sum
+// formed inside the same inline assembly, so that none of the per-instruction
+// values is kept in a register across a loop (a tile's dozens of destinations
+// and row offsets would otherwise be hoisted and spill).  The whole offset is
+// per-lane, so the buffer range check covers it.  The scalar adds write SCC,
+// which the clobber list declares.
+template <int I, int LDSOFF>
+__device__ __forceinline__ void dl_load16_idx(const Rsrc& r, int lds_base, int voff, int vstep, int soff) {
+  int t, st;
+  asm volatile("s_mul_i32 %1, %3, %4\n\t"
+               "v_add_u32 %0, %1, %2\n\t"
+               "s_add_u32 m0, %5, %6\n\t"
+               "s_nop 0\n\t"
+               "buffer_load_dwordx4 %0, %7, %8 offen lds"
+               : "=&v"(t), "=&s"(st)
+               : "v"(voff), "s"(vstep), "i"(I), "s"(lds_base), "i"(LDSOFF), "s"(r.v), "s"(soff)
+               : "memory", "scc");
+}
+
+template <int I, int LDSOFF>
+__device__ __forceinline__ void dl_load4_idx(const Rsrc& r, int lds_base, int voff, int vstep, int vadd) {
+  int t, st;
+  asm volatile("s_mul_i32 %1, %3, %4\n\t"
+               "s_add_u32 %1, %1, %5\n\t"
+               "v_add_u32 %0, %1, %2\n\t"
+               "s_add_u32 m0, %6, %7\n\t"
+               "s_nop 0\n\t"
+               "buffer_load_dword %0, %8, 0 offen lds"
+               : "=&v"(t), "=&s"(st)
+               : "v"(voff), "s"(vstep), "i"(I), "s"(vadd), "s"(lds_base), "i"(LDSOFF), "s"(r.v)
+               : "memory", "scc");
+}
+
 // 16 bytes per lane from memory into registers.  Inline assembly like the LDS-DMA
 // loads above, for the same reason: the caller counts its loads (s_waitcnt
 // vmcnt) and ties the result registers to its own wait (`tie_after_wait`); the
@@ -225,6 +259,23 @@ __device__ __forceinline__ v4i lds_read16(int addr) {
   v4i v;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
+}
+
+// As lds_read16, at address (addr ^ XOR) + OFF: the XOR is part of the same
+// inline assembly, so it is computed where the read is issued and holds no
+// register across a loop.
+template <int OFF, int XOR>
+__device__ __forceinline__ v4i lds_read16_xor(int addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS instruction offsets are 16 bits");
+  if constexpr (XOR == 0) {
+    return lds_read16<OFF>(addr);
+  } else {
+    v4i v;
+    int t;
+    asm volatile("v_xor_b32 %1, %3, %2\n\tds_read_b128 %0, %1 offset:%4"
+                 : "=v"(v), "=&v"(t) : "v"(addr), "i"(XOR), "i"(OFF));
+    return v;
+  }
 }
 
 template <int OFF>

@@ -12,7 +12,7 @@
 // workspace), so both kinds give identical bits (PR #57977, Test Result).
 //
 // Tiling.  A workgroup of four waves owns BN weight rows x BM tokens and walks K
-// in 64-deep half steps.  Wave (wn, wm) owns a (BN / WAVES_N) x (BM / WAVES_M)
+// in 128-deep steps, each two 64-deep MFMA half steps.  Wave (wn, wm) owns a (BN / WAVES_N) x (BM / WAVES_M)
 // sub-tile of 32 x 32 MFMA tiles, TN x TM of them.
 //
 // Token rows past M: the row part of every activation offset is in the per-lane
@@ -37,38 +37,43 @@ struct BigCfg {
 // ---------------------------------------------------------------------------
 // Both operands are codes, so they go from memory straight into LDS
 // (buffer_load_dwordx4 ... lds: lane l of an instruction writes 16 bytes at
-// LDS base + 16 l) and no registers stage them.  That frees enough LDS to keep
-// four half-step stages (64-deep: 256 rows x 64 bytes per operand = 16 KB), so
-// the loads of stage t+3 are issued while stage t is multiplied -- three stages
-// of latency cover instead of one.
+// LDS base + 16 l) and no registers stage them.  LDS holds two K-steps
+// (128-deep: 256 + 256 rows x 128 bytes = 64 KB each), so the loads of step k+2
+// go out while step k is multiplied.
 //
-// Stage layout of one operand: row tile T (32 rows) is a 2 KB block of 128
-// 16-byte slots; chunk cc (0..3, = 2h + q) of row r sits in slot
-//     4r + (cc ^ g(r)),   g(r) = ((r >> 1) ^ (r >> 3)) & 1 | ((r >> 2) & 1) << 1,
-// so one load instruction (64 lanes = 16 rows x 4 chunks, row-contiguous 64 bytes
-// each) fills 1 KB of consecutive slots, and the 16 lanes of one fragment read
-// (16 rows, one chunk) hit 16 different 16-byte bank groups (8 for any 8 rows).
-// The fragment of lane (i, q) is chunk q (dwords 0-3) and chunk 2 + q (dwords
-// 4-7) of row i: operand bytes 16q .. 16q+15 and 32+16q .. 32+16q+15 of the half
-// step, the MFMA's lane layout.
-__device__ __forceinline__ int dl_g(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
+// Each load instruction covers eight rows x 128 bytes: every 128-byte line it
+// touches is read whole, once.  (Four-row-per-64-byte-half layouts -- one line
+// requested twice, a K half-step apart -- took the vector L1 twice the requests
+// for the same bytes and ran the loads 25% slower.)
+//
+// Step layout of one operand: row r occupies 128 bytes (eight 16-byte slots);
+// chunk c (0..7: bytes 16c .. 16c+15 of the row's 128 K values) sits in slot
+//     c ^ f(r),   f(r) = (r >> 1) & 7,
+// so one load instruction (64 lanes = 8 rows x 8 slots) fills 1 KB of
+// consecutive slots, and the 16 lanes of one fragment read (16 rows, one chunk)
+// hit 16 different 16-byte bank groups.  The fragment of lane (i, q) for half step
+// h is chunk 4h + q (dwords 0-3) and chunk 4h + 2 + q (dwords 4-7) of row i:
+// operand bytes 16q .. 16q+15 and 32+16q .. 32+16q+15 of the half step, the
+// MFMA's lane layout.  Since f(r) < 8, the two halves of a step differ by
+// address bit 6 only (slot bit 2).
+__device__ __forceinline__ int dl_f(int r) { return (r >> 1) & 7; }
 
-// LDS of the direct-to-LDS kernel: four half-step stages of operand data, then
-// two buffers of scale words.  A scale buffer holds the words of four K-steps
-// (eight stages) for every row of both operands, 16 bytes per row, so the scale
-// loads touch each row once per four K-steps instead of once per stage: loads of
-// one word per row cost an L2 request per row, as many as the operand data.
-// Stages 0-1 and 2-3 each fit one 64 KB window of the LDS instruction offset
-// field, so one per-lane base address per window serves every fragment read.
+// LDS of the direct-to-LDS kernel: two K-step buffers of operand data (weight
+// rows, then token rows), then two buffers of scale words.  A scale buffer holds
+// the words of four K-steps for every row of both operands, 16 bytes per row, so
+// the scale loads touch each row once per four K-steps instead of once per step:
+// loads of one word per row cost an L2 request per row, as many as the operand
+// data.  Each K-step buffer gets its own per-lane read bases (the LDS instruction
+// offset field spans 64 KB).
 template <class C>
 struct DlLds {
-  static constexpr int DATA = (C::BN + C::BM) * 64;
-  static constexpr int W = 0, X = C::BN * 64;              // within a stage's data
+  static constexpr int DATA = (C::BN + C::BM) * 128;
+  static constexpr int W = 0, X = C::BN * 128;            // within a step's data
   static constexpr int SROWS = C::BN + C::BM;              // weight rows, then token rows
   static constexpr int SBUF = SROWS * 16;
-  static constexpr int SCALES = 4 * DATA;
-  static constexpr int BYTES = 4 * DATA + 2 * SBUF;
-  static_assert(2 * DATA <= 65536, "two stages per 64 KB window");
+  static constexpr int SCALES = 2 * DATA;
+  static constexpr int BYTES = 2 * DATA + 2 * SBUF;
+  static_assert(DATA <= 65536, "tile offsets of a step within one LDS offset window");
   static_assert(BYTES <= 160 * 1024, "LDS of one CU");
 };
 
@@ -77,10 +82,11 @@ struct DlLds {
 template <class C, int OUT>
 __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g, int64_t n0, int64_t m0) {
   static_assert(C::NW == 4, "four waves");
-  constexpr int WI = C::BN / 64;                 // weight load instructions per wave and stage
-  constexpr int XI = C::BM / 64;                 // activation load instructions per wave and stage
-  constexpr int L = WI + XI;                     // loads per wave and stage
+  constexpr int WI = C::BN / 32;                 // weight load instructions per wave and K-step (8 rows each)
+  constexpr int XI = C::BM / 32;                 // activation load instructions per wave and K-step
+  constexpr int L = WI + XI;                     // loads per wave and K-step
   constexpr int SI = (C::BN + C::BM) / 64;       // scale-word load instructions per wave and scale group
+  constexpr int NT = C::TN + C::TM;              // fragment tiles per half step
   using Lds = DlLds<C>;
 
   // the wave index is uniform: keep it in a scalar register (load offsets and LDS bases derive from it)
@@ -88,65 +94,66 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
   const int ksteps = (int)(p.K / 128);
-  const int nst = 2 * ksteps;                    // half-step stages, 64 deep
   const int64_t rows_left = p.M - m0;
   const int64_t m_rows = rows_left < C::BM ? rows_left : C::BM;
   const int ldw = (int)p.K, ldx = (int)p.ld_x, ldxs = (int)(p.ld_xsf * 4);
   const Rsrc rw = make_rsrc_sgpr(p.w + ((int64_t)g * p.N + n0) * p.K, (int64_t)C::BN * p.K);
   const Rsrc rws = make_rsrc_sgpr(p.w_sf + ((int64_t)g * p.N + n0) * ksteps, (int64_t)C::BN * ksteps * 4);
   const Rsrc rnull = make_rsrc_sgpr(p.w, 0);
-  // Activations: every load instruction covers 16 token rows and gets its own
-  // buffer resource starting at its first row and ending at row m_rows; the
-  // per-lane offset holds the row within the instruction, and the range check --
-  // which sees the per-lane offset only -- turns rows past M into zeros without
-  // reading them.
+  // Activations: one buffer resource from the tile's first token row to row M;
+  // the row part of every activation offset is in the per-lane offset, which the
+  // range check covers (the scalar offset is not checked), so rows past M arrive
+  // as zeros without being read.
   const int xcol0 = (int)((int64_t)g * p.K);
   const int xsfcol0 = g * ksteps * 4;
   const uint8_t* x_tile = static_cast<const uint8_t*>(p.x) + m0 * ldx;
   const int32_t* xsf_tile = p.x_sf + m0 * p.ld_xsf;
-  auto x_rsrc = [&](int row0) {
-    const int64_t rows = m_rows - row0;
-    return make_rsrc_sgpr(x_tile + (int64_t)row0 * ldx, rows > 0 ? rows * ldx : 0);
-  };
-  auto xs_rsrc = [&](int row0) {
-    const int64_t rows = m_rows - row0;
-    return make_rsrc_sgpr(xsf_tile + (int64_t)row0 * p.ld_xsf, rows > 0 ? rows * ldxs : 0);
-  };
+  const Rsrc rx = make_rsrc_sgpr(x_tile, m_rows * ldx);
+  const Rsrc rxs = make_rsrc_sgpr(xsf_tile, m_rows * ldxs);
 
-  // per-lane parts of the load offsets (the same for every stage and instruction)
-  const int lr = lane >> 2, lc = (lane & 3) ^ dl_g(lane >> 2);
-  const int vw = lr * ldw + lc * 16, vx = lr * ldx + lc * 16;
-  // scale words: lane l reads word l % 4 of the group's four in row l / 4 of the instruction's 16 rows
-  const int vws = lr * ksteps * 4 + (lane & 3) * 4, vxs = lr * ldxs + xsfcol0 + (lane & 3) * 4;
+  // Per-lane parts of the load offsets (the same for every step and instruction):
+  // instruction d of a wave covers rows 8n .. 8n+7, n = 4d + wave, so its offset is
+  // the wave's base (rows 8 wave + l / 8) plus d x 32 rows.  Lane l fills slot l % 8
+  // of its row, so it reads chunk (l % 8) ^ f(row); f's top bit is the parity of n,
+  // which is the wave's parity.
+  const int lr = lane >> 3;
+  const int lc = (lane & 7) ^ (((wave & 1) << 2) | (lr >> 1));
+  const int vw = (8 * wave + lr) * ldw + lc * 16, vx = (8 * wave + lr) * ldx + lc * 16;
+  const int sw_step = 32 * ldw, sx_step = 32 * ldx;
+  const int lds_ops = (int)lds_addr(smem) + wave * 1024;
+  // scale words: instruction j covers rows 16n .. 16n+15 (n = 4j + wave) of the
+  // weight-then-token row list; lane l reads word l % 4 of the group's four in row l / 4
+  const int slr = lane >> 2;
+  const int vws = (16 * wave + slr) * ksteps * 4 + (lane & 3) * 4;
+  const int vxs = (16 * wave + slr) * ldxs + xsfcol0 + (lane & 3) * 4;
+  const int sws_step = 64 * ksteps * 4, sxs_step = 64 * ldxs;
+  const int lds_sc = (int)lds_addr(smem) + Lds::SCALES + wave * 256;
 
-  // Load instruction d (< WI: weights, then tokens) of stage t into stage buffer
-  // b (= t % 4).  With `on` false the instruction gets a resource of zero bytes:
-  // every lane is out of range, nothing is read and the buffer receives zeros --
-  // a no-op for a buffer nobody reads, issued without a branch.
-  auto issue_one = [&](auto d_tag, int b, int t, bool on) {
-    constexpr int d = decltype(d_tag)::value;
-    uint8_t* data = smem + b * Lds::DATA;
-    const int kt = t >> 1, ks = t & 1;
-    if constexpr (d < WI) {
-      const int n = 4 * d + wave;                 // rows 16n .. 16n+15
-      dl_load16(on ? rw : rnull, data + Lds::W + n * 1024, vw, 16 * n * ldw + kt * 128 + ks * 64);
-    } else {
-      const int n = 4 * (d - WI) + wave;
-      dl_load16(on ? x_rsrc(16 * n) : rnull, data + Lds::X + n * 1024, vx, xcol0 + kt * 128 + ks * 64);
-    }
+  // Load instruction d (< WI: weights, then tokens) of K-step k into step buffer
+  // B.  With `on` false the instruction gets a resource of zero bytes: every lane
+  // is out of range, nothing is read and the buffer receives zeros -- a no-op for
+  // a buffer nobody reads, issued without a branch.
+  auto issue_one = [&](auto d_tag, auto b_tag, int k, bool on) {
+    constexpr int d = decltype(d_tag)::value, B = decltype(b_tag)::value;
+    if constexpr (d < WI)
+      dl_load16_idx<d, B * Lds::DATA + Lds::W + 4096 * d>(on ? rw : rnull, lds_ops, vw, sw_step, k * 128);
+    else
+      dl_load16_idx<d - WI, B * Lds::DATA + Lds::X + 4096 * (d - WI)>(on ? rx : rnull, lds_ops, vx, sx_step,
+                                                                       xcol0 + k * 128);
   };
-  auto issue = [&](int b, int t) { static_for<L>([&](auto d_tag) { issue_one(d_tag, b, t, t < nst); }); };
-  // scale words of group s (K-steps 4s .. 4s+3) into scale buffer s % 2.  Words
-  // past the end of a row (last group of a K range that is not a multiple of
-  // four steps) are never used; the whole offset is in voffset, so the range
+  // scale words of group s (K-steps 4s .. 4s+3) into scale buffer SB = s % 2.
+  // Words past the end of a row (last group of a K range that is not a multiple
+  // of four steps) are never used; the whole offset is per-lane, so the range
   // check also covers them.  With `on` false: zero-byte resources, as above.
-  auto issue_scales = [&](int s, bool on) {
-    uint8_t* sc = smem + Lds::SCALES + (s & 1) * Lds::SBUF;
+  auto issue_scales = [&](auto sb_tag, int s, bool on) {
+    constexpr int SB = decltype(sb_tag)::value;
     static_for<SI>([&](auto j_tag) {
       constexpr int j = decltype(j_tag)::value;
-      const int n = 4 * j + wave;                 // rows 16n .. 16n+15 of the weight-then-token row list
-      if constexpr (4 * j < C::BN / 16) dl_load4(on ? rws : rnull, sc + n * 256, vws + 16 * n * ksteps * 4 + 16 * s, 0);
-      else dl_load4(on ? xs_rsrc(16 * n - C::BN) : rnull, sc + n * 256, vxs + 16 * s, 0);
+      constexpr int LO = SB * Lds::SBUF + 1024 * j;
+      if constexpr (4 * j < C::BN / 16)
+        dl_load4_idx<j, LO>(on ? rws : rnull, lds_sc, vws, sws_step, 16 * s);
+      else
+        dl_load4_idx<j - C::BN / 64, LO>(on ? rxs : rnull, lds_sc, vxs, sxs_step, 16 * s);
     });
   };
 
@@ -156,170 +163,191 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
 #pragma unroll
     for (int b = 0; b < C::TM; ++b) acc[a][b] = zero16();
 
-  // MFMA operands of one stage, held in registers: while the MFMAs of stage t run
-  // on one set, the LDS reads of stage t+1 fill the other.
+  // MFMA operands of the two half steps of a K-step, held in registers: f0 (first
+  // half) and f1 (second half).
   struct Frags {
     v8i fw[C::TN], fx[C::TM];
     int sw[C::TN], sx[C::TM];
   };
   // The fragment reads are inline assembly with explicit base registers and
-  // constant offsets: a handful of per-lane bases serve every stage and tile (left
-  // to itself the compiler keeps one address register per stage and tile, runs
+  // constant offsets: a handful of per-lane bases serve every step and tile (left
+  // to itself the compiler keeps one address register per step and tile, runs
   // out of registers and spills -- and a spill reload in this loop would wait for
   // every load in flight).  The compiler does not see these reads complete, so
-  // wait_early() and wait_late() wait for them and tie the registers to those waits.
-  const int gi = dl_g(i);
-  const int off_lo = 64 * i + 16 * (q ^ gi), off_hi = 64 * i + 16 * ((2 + q) ^ gi);
+  // the waits below wait for them and tie the registers to those waits.
+  const int fi = dl_f(i);
   const int base = (int)lds_addr(smem);
-  constexpr int WIN = 2 * Lds::DATA;              // stages 2-3 start here
-  const int aw_lo = base + wn * C::TN * 2048 + off_lo, aw_hi = base + wn * C::TN * 2048 + off_hi;
-  const int ax_lo = base + wm * C::TM * 2048 + off_lo, ax_hi = base + wm * C::TM * 2048 + off_hi;
-  const int aw_lo1 = aw_lo + WIN, aw_hi1 = aw_hi + WIN, ax_lo1 = ax_lo + WIN, ax_hi1 = ax_hi + WIN;
+  // read bases per step buffer: chunk q of row i (lo, first half step); chunk
+  // 2 + q is that address ^ 32, and the second half step's chunks are ^ 64
+  int aw0[2], ax0[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    aw0[b] = base + b * Lds::DATA + Lds::W + wn * C::TN * 4096 + 128 * i + 16 * (q ^ fi);
+    ax0[b] = base + b * Lds::DATA + Lds::X + wm * C::TM * 4096 + 128 * i + 16 * (q ^ fi);
+  }
   const int aws = base + Lds::SCALES + (wn * C::TN * 32 + i) * 16;
   const int axs = base + Lds::SCALES + (C::BN + wm * C::TM * 32 + i) * 16;
-  // Fragment read r of stage J (mod 16) of the unrolled loop: r < TN is weight
-  // tile r, then token tile r - TN; each is a scale word and two 16-byte halves.
-  // Stage J lives in data buffer J % 4 and scale buffer J / 8, scale word (J % 8) / 2.
-  auto read_tile = [&](auto r_tag, auto stage_tag, Frags& F) {
-    constexpr int r = decltype(r_tag)::value, J = decltype(stage_tag)::value;
-    constexpr int B = J % 4, SB = (J / 8) * Lds::SBUF + ((J % 8) / 2) * 4;
-    constexpr int D = (B & 1) * Lds::DATA;              // within the 64 KB window of stage buffer B
+  // Fragment read r of half step H of K-step J (mod 8) of the unrolled loop: r < TN
+  // is weight tile r, then token tile r - TN; each is a scale word and two 16-byte
+  // halves.  K-step J lives in step buffer J % 2 and scale buffer J / 4, scale word J % 4.
+  auto read_tile = [&](auto r_tag, auto j_tag, auto h_tag, Frags& F) {
+    constexpr int r = decltype(r_tag)::value, J = decltype(j_tag)::value, H = decltype(h_tag)::value;
+    constexpr int B = J % 2, SB = (J / 4) * Lds::SBUF + (J % 4) * 4;
     if constexpr (r < C::TN) {
-      const int wl = (B >> 1) ? aw_lo1 : aw_lo, wh = (B >> 1) ? aw_hi1 : aw_hi;
       F.sw[r] = lds_read4<SB + r * 512>(aws);
-      F.fw[r] = join8(lds_read16<D + Lds::W + r * 2048>(wl), lds_read16<D + Lds::W + r * 2048>(wh));
+      F.fw[r] = join8(lds_read16_xor<r * 4096, 64 * H>(aw0[B]), lds_read16_xor<r * 4096, 64 * H + 32>(aw0[B]));
     } else {
       constexpr int c = r - C::TN;
-      const int xl = (B >> 1) ? ax_lo1 : ax_lo, xh = (B >> 1) ? ax_hi1 : ax_hi;
       F.sx[c] = lds_read4<SB + c * 512>(axs);
-      F.fx[c] = join8(lds_read16<D + Lds::X + c * 2048>(xl), lds_read16<D + Lds::X + c * 2048>(xh));
+      F.fx[c] = join8(lds_read16_xor<c * 4096, 64 * H>(ax0[B]), lds_read16_xor<c * 4096, 64 * H + 32>(ax0[B]));
     }
   };
-  // Read order of a stage's tiles: what the first half of the MFMAs needs (weight
-  // tiles 0 .. TN/2-1 and every token tile, in the order those MFMAs use them)
-  // first, the weight tiles of the second half last; a step then waits only for
-  // the first group before it starts, and for the rest before its second half.
+  // Read order of a half step's tiles: what the first half of its MFMAs needs
+  // (weight tiles 0 .. TN/2-1 and every token tile, in the order those MFMAs use
+  // them) first, the weight tiles of the second half last.
   constexpr auto order = [](int k) constexpr {
     if (k == 0) return 0;                                   // W0
     if (k <= C::TM) return C::TN + k - 1;                   // X0 .. X(TM-1)
     return k - C::TM;                                       // W1 .. W(TN-1)
   };
+  static_assert(C::TN == 4 && C::TM <= 4, "register ties below list the tiles by name");
   constexpr int LATE_LDS_OPS = 3 * (C::TN / 2);             // scale word + two halves per late tile
-  auto read = [&](auto stage_tag, Frags& F) {
-    static_for<C::TN + C::TM>([&](auto k_tag) {
-      read_tile(std::integral_constant<int, order(decltype(k_tag)::value)>{}, stage_tag, F);
-    });
+  auto shift_scales = [&](Frags& F, int a0, int a1, bool x) {
+    for (int a = a0; a < a1; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
+    if (x)
+      for (int c = 0; c < C::TM; ++c) F.sx[c] = (int)((uint32_t)F.sx[c] >> (8 * q));
   };
-  // waits for the tiles of the first half (all but the last LATE_LDS_OPS LDS reads),
-  // then for the rest; each ties the registers it covers to its wait
-  auto wait_early = [&](Frags& F) {
-    static_assert(C::TN == 4 && C::TM <= 4, "register ties below list the tiles by name");
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(F.fw[0]), "+v"(F.fw[1]) : "n"(LATE_LDS_OPS));
-    asm volatile("" : "+v"(F.sw[0]), "+v"(F.sw[1]));
+  auto tie_x = [&](Frags& F) {
     if constexpr (C::TM == 4)
       asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.fx[2]), "+v"(F.fx[3]), "+v"(F.sx[0]), "+v"(F.sx[1]),
                    "+v"(F.sx[2]), "+v"(F.sx[3]));
     else
       asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.sx[0]), "+v"(F.sx[1]));
-#pragma unroll
-    for (int a = 0; a < C::TN / 2; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
-#pragma unroll
-    for (int c = 0; c < C::TM; ++c) F.sx[c] = (int)((uint32_t)F.sx[c] >> (8 * q));
   };
-  auto wait_late = [&](Frags& F) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F.fw[2]), "+v"(F.fw[3]), "+v"(F.sw[2]), "+v"(F.sw[3]));
-#pragma unroll
-    for (int a = C::TN / 2; a < C::TN; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
+  // f0 of a K-step is read last (end of the previous K-step), its late weight
+  // tiles last of all: wait for all but those
+  auto wait_f0_early = [&](Frags& F) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(F.fw[0]), "+v"(F.fw[1]) : "n"(LATE_LDS_OPS));
+    asm volatile("" : "+v"(F.sw[0]), "+v"(F.sw[1]));
+    tie_x(F);
+    shift_scales(F, 0, C::TN / 2, true);
   };
-  // half H (0, 1) of the TN x TM MFMAs of a stage; KS = stage parity (which 64 bytes of the K-step)
-  auto mma = [&](const Frags& F, auto ks_tag, auto half_tag) {
-    constexpr int KS = decltype(ks_tag)::value, H = decltype(half_tag)::value;
-#pragma unroll
-    for (int a = H * C::TN / 2; a < (H + 1) * C::TN / 2; ++a)
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_scaled<2 * KS>(F.fw[a], F.fx[b], acc[a][b], F.sw[a], F.sx[b]);
+  // everything: f0's late tiles and all of f1
+  auto wait_f0_late_f1 = [&](Frags& F0, Frags& F1) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F0.fw[2]), "+v"(F0.fw[3]), "+v"(F0.sw[2]), "+v"(F0.sw[3]));
+    asm volatile("" : "+v"(F1.fw[0]), "+v"(F1.fw[1]), "+v"(F1.fw[2]), "+v"(F1.fw[3]), "+v"(F1.sw[0]), "+v"(F1.sw[1]),
+                 "+v"(F1.sw[2]), "+v"(F1.sw[3]));
+    tie_x(F1);
+    shift_scales(F0, C::TN / 2, C::TN, false);
+    shift_scales(F1, 0, C::TN, true);
   };
 
-  // Stage t lives in data buffer t % 4, its scale words in scale buffer (t / 8) % 2,
-  // and its operands in Frags t % 2.  One step: first half of stage t's MFMAs; then
-  // -- once this wave's loads of stage t+1 are complete (stages t+2, t+3 may still
-  // be in flight) -- a barrier makes every wave's stage t+1 visible and, since
-  // every wave has consumed its stage-t operands by then, frees data buffer t % 4
-  // for the loads of stage t+4 (and, at t = 8s, scale buffer (s+1) % 2, last used
-  // by stages up to 8s-1, for scale group s+1).  The second half of stage t's
-  // MFMAs follows, with the LDS reads of stage t+1 and the loads of stage t+4
-  // slotted between them: a wave issues in order, so a load instruction that has
-  // to wait for the memory pipeline then holds up at most one MFMA's worth of
-  // issue, not a whole half-stage.
-  //
-  // A step has no branches: a branch would split the scheduling region and let
-  // the compiler regroup the MFMAs.  Every step issues the loads of stage t+4 and,
-  // at t = 8s, of scale group s+1 -- switched off (zero-byte resources) where
-  // those do not exist -- so the number of loads issued after stage t+1's is the
-  // same constant at every step, and the last step's reads fetch a buffer that
-  // is never used.
-  using H0 = std::integral_constant<int, 0>;
-  constexpr int NMF = C::TN / 2 * C::TM;             // MFMAs per half-stage
-  static_assert(C::TN + C::TM == L, "one fragment read per load instruction");
-  constexpr int PER = (2 * L + NMF - 1) / NMF;       // reads and loads slotted after each MFMA
-  auto step = [&](Frags& cur, Frags& nxt, auto stage_tag, int t) {
-    constexpr int J = decltype(stage_tag)::value;     // t % 16
-    constexpr int KS = J & 1;
-    wait_early(cur);
-    mma(cur, std::integral_constant<int, KS>{}, H0{});
-    __builtin_amdgcn_sched_barrier(0);
-    // loads issued after stage t+1's: stages t+2 and t+3, plus scale group s+1
-    // when it went out with stage 8s+4, one of those two
-    wait_vmcnt<2 * L + ((J % 8 == 1 || J % 8 == 2) ? SI : 0)>();
-    asm volatile("s_barrier" ::: "memory");
-    if constexpr (J % 8 == 0) issue_scales(t / 8 + 1, 8 * (t / 8 + 1) < nst);
-    const bool refill = t + 4 < nst;
-    wait_late(cur);
-    __builtin_amdgcn_sched_barrier(0);
+  // One K-step k (J = k % 8) in four quarters of NMF MFMAs each, f0's weight tiles
+  // 0 .. TN/2-1, then TN/2 .. TN-1, then f1's likewise:
+  //   A1: f0's first MFMAs; reads of all of f1 (step buffer k % 2, already visible)
+  //       slotted between them.  Then every wave waits for its reads and a barrier
+  //       frees step buffer k % 2 for the loads of step k+2 (and, at k = 4s, scale
+  //       buffer (s+1) % 2, last used by steps up to 4s-1, for scale group s+1).
+  //   A2, B1, B2: the rest of the MFMAs with the L loads of step k+2 spread evenly
+  //       between them (one memory pipeline per CU: loads issued in a burst queue
+  //       faster than it accepts them, and a wave waiting to issue a load issues no
+  //       MFMA either).
+  //   Before B2, each wave waits for its loads of step k+1 (the ones issued in the
+  //       three quarters before the previous B2 ended), and a barrier makes every
+  //       wave's step k+1 visible; B2 then also reads f0 of step k+1.
+  // A step has no branches: a branch would split the scheduling region and let the
+  // compiler regroup the MFMAs.  Every step issues the loads of step k+2 and, at
+  // k = 4s, of scale group s+1 -- switched off (zero-byte resources) where those do
+  // not exist -- so the number of loads issued after step k+1's is a constant, and
+  // the last step's reads fetch a buffer that is never used.
+  constexpr int NMF = C::TN / 2 * C::TM;             // MFMAs per quarter
+  constexpr auto load_slot = [](int d) constexpr { return d * 3 * NMF / L; };   // MFMA of A2, B1, B2 it follows
+  constexpr int P12 = (2 * L + 2) / 3;               // loads in A2 and B1: load_slot(d) < 2 NMF <=> 3d < 2L
+  Frags f0, f1;
+  auto mfma_q = [&](auto j_tag, auto quarter_tag, int k) {
+    constexpr int J = decltype(j_tag)::value, Q = decltype(quarter_tag)::value;   // Q: 0 = A1 .. 3 = B2
+    constexpr int H = Q / 2;
+    Frags& F = H == 0 ? f0 : f1;
+    const bool on = k + 2 < ksteps;
     static_for<NMF>([&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
-      constexpr int a = C::TN / 2 + m / C::TM, b = m % C::TM;
-      acc[a][b] = mfma_scaled<2 * KS>(cur.fw[a], cur.fx[b], acc[a][b], cur.sw[a], cur.sx[b]);
+      constexpr int a = (Q % 2) * (C::TN / 2) + m / C::TM, b = m % C::TM;
+      acc[a][b] = mfma_scaled<2 * H>(F.fw[a], F.fx[b], acc[a][b], F.sw[a], F.sx[b]);
       __builtin_amdgcn_sched_barrier(0);
-      static_for<PER>([&](auto k_tag) {
-        constexpr int o = m * PER + decltype(k_tag)::value;   // even: read o/2, odd: load o/2
-        if constexpr (o < 2 * L) {
-          if constexpr (o % 2 == 0)
-            read_tile(std::integral_constant<int, order(o / 2)>{}, std::integral_constant<int, (J + 1) % 16>{}, nxt);
-          else
-            issue_one(std::integral_constant<int, o / 2>{}, J % 4, t + 4, refill);
-        }
-      });
+      if constexpr (Q == 0 || Q == 3) {
+        static_for<NT>([&](auto t_tag) {
+          constexpr int t = decltype(t_tag)::value;
+          if constexpr (t * NMF / NT == m) {
+            if constexpr (Q == 0)
+              read_tile(std::integral_constant<int, order(t)>{}, j_tag, std::integral_constant<int, 1>{}, f1);
+            else
+              read_tile(std::integral_constant<int, order(t)>{}, std::integral_constant<int, (J + 1) % 8>{},
+                        std::integral_constant<int, 0>{}, f0);
+          }
+        });
+      }
+      if constexpr (Q > 0) {
+        static_for<L>([&](auto d_tag) {
+          constexpr int d = decltype(d_tag)::value;
+          if constexpr (load_slot(d) == (Q - 1) * NMF + m)
+            issue_one(d_tag, std::integral_constant<int, J % 2>{}, k + 2, on);
+        });
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
+  auto kstep = [&](auto j_tag, int k) {
+    constexpr int J = decltype(j_tag)::value;
+    wait_f0_early(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(j_tag, std::integral_constant<int, 0>{}, k);
+    wait_f0_late_f1(f0, f1);
+    asm volatile("s_barrier" ::: "memory");
+    if constexpr (J % 4 == 0)      // group k/4 + 1 = k0/4 + J/4 + 1, k0 a multiple of 8
+      issue_scales(std::integral_constant<int, (J / 4 + 1) % 2>{}, k / 4 + 1, 4 * (k / 4 + 1) < ksteps);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(j_tag, std::integral_constant<int, 1>{}, k);
+    mfma_q(j_tag, std::integral_constant<int, 2>{}, k);
+    // loads issued after step k+1's last one: A2 and B1 of this step, and scale
+    // group s+1 when it went out at the start of A2 (k = 4s)
+    wait_vmcnt<P12 + (J % 4 == 0 ? SI : 0)>();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(j_tag, std::integral_constant<int, 3>{}, k);
+  };
 
-  Frags f0, f1;
-  issue_scales(0, true);
-  static_for<4>([&](auto b_tag) { issue(decltype(b_tag)::value, decltype(b_tag)::value); });   // off past nst
-  wait_vmcnt<3 * L>();
+  issue_scales(std::integral_constant<int, 0>{}, 0, true);
+  static_for<L>([&](auto d_tag) { issue_one(d_tag, std::integral_constant<int, 0>{}, 0, true); });
+  static_for<L>([&](auto d_tag) { issue_one(d_tag, std::integral_constant<int, 1>{}, 1, 1 < ksteps); });
+  wait_vmcnt<L>();                                 // scale group 0 and step 0
   asm volatile("s_barrier" ::: "memory");
-  read(std::integral_constant<int, 0>{}, f0);
-  for (int t0 = 0; t0 < nst; t0 += 16) {
-    static_for<8>([&](auto pair_tag) {           // stages come in pairs: nst is even
-      constexpr int P = decltype(pair_tag)::value;
-      if (P == 0 || t0 + 2 * P < nst) {
-        step(f0, f1, std::integral_constant<int, 2 * P>{}, t0 + 2 * P);
-        step(f1, f0, std::integral_constant<int, 2 * P + 1>{}, t0 + 2 * P + 1);
-      }
+  static_for<NT>([&](auto t_tag) {
+    read_tile(std::integral_constant<int, order(decltype(t_tag)::value)>{}, std::integral_constant<int, 0>{},
+              std::integral_constant<int, 0>{}, f0);
+  });
+  for (int k0 = 0; k0 < ksteps; k0 += 8) {
+    static_for<8>([&](auto j_tag) {
+      constexpr int J = decltype(j_tag)::value;
+      if (J == 0 || k0 + J < ksteps) kstep(j_tag, k0 + J);
     });
   }
+  // The last step's reads of f0 (of a step that does not exist; f1's reads were
+  // waited for within the step) and the switched-off loads -- which still write zeros into the step buffers that the
+  // epilogue reuses -- have all landed before the barrier below.
+  wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f0.fw[0]), "+v"(f0.fw[1]), "+v"(f0.fw[2]), "+v"(f0.fw[3]), "+v"(f0.sw[0]),
+               "+v"(f0.sw[1]), "+v"(f0.sw[2]), "+v"(f0.sw[3]));
+  tie_x(f0);
 
-  // Epilogue through LDS, one 32-token block at a time.  Every wave has waited
-  // for its last fragment reads before this barrier, so the stage buffers are free.
+  // Epilogue through LDS, one 32-token block at a time.
   // The lane's row i and half q (and so the lane index) are taken back from a base
   // address that lives through the loop anyway, so that nothing the epilogue
   // derives from them is computed early and kept alive across the loop.
   __syncthreads();
-  int aw = aw_lo;
+  int aw = aw0[0];
   asm volatile("" : "+v"(aw));                     // opaque: keeps the compiler from reusing the original i
-  const int i_e = (aw - base - wn * C::TN * 2048) >> 6;
-  const int q_e = ((aw >> 4) & 3) ^ dl_g(i_e);
+  const int i_e = ((aw - base - wn * C::TN * 4096) >> 7) & 31;
+  const int q_e = ((aw >> 4) & 7) ^ dl_f(i_e);
   static_assert(4 * EpiLds<C::TN>::BYTES <= Lds::BYTES, "epilogue blocks of the four waves");
   uint8_t* chunk = smem + wave * EpiLds<C::TN>::BYTES;
   const int64_t nb = (int64_t)g * p.N + n0 + wn * C::TN * 32;
@@ -327,6 +355,9 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   for (int b = 0; b < C::TM; ++b) {
 #pragma unroll
     for (int a = 0; a < C::TN; ++a) {
+      // each tile stays in accumulator registers until its turn (copied out all at
+      // once, the tiles would not fit the general registers)
+      asm volatile("" : "+a"(acc[a][b]));
       epi_write_tile<C::TN>(chunk, acc[a][b], a, i_e, q_e);
       __builtin_amdgcn_sched_barrier(0);
     }
