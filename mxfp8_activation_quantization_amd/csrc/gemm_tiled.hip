@@ -25,9 +25,12 @@
 
 namespace mx {
 
-template <int BN_, int BM_, int WAVES_N_, int WAVES_M_>
+// BN weight rows x BM tokens per workgroup, WAVES_N x WAVES_M waves, NB K-step
+// buffers in LDS (loads run NB - 1 steps ahead of the multiplications).
+template <int BN_, int BM_, int WAVES_N_, int WAVES_M_, int NB_ = 2>
 struct BigCfg {
-  static constexpr int BN = BN_, BM = BM_, WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
+  static constexpr int BN = BN_, BM = BM_, WAVES_N = WAVES_N_, WAVES_M = WAVES_M_, NB = NB_;
+  static_assert(NB == 2 || NB == 4, "step buffers cycle within the eight unrolled K-steps");
   static constexpr int NW = WAVES_N * WAVES_M, THREADS = 64 * NW;
   static constexpr int WN = BN / WAVES_N, WM = BM / WAVES_M;
   static constexpr int TN = WN / 32, TM = WM / 32;
@@ -37,9 +40,10 @@ struct BigCfg {
 // ---------------------------------------------------------------------------
 // Both operands are codes, so they go from memory straight into LDS
 // (buffer_load_dwordx4 ... lds: lane l of an instruction writes 16 bytes at
-// LDS base + 16 l) and no registers stage them.  LDS holds two K-steps
-// (128-deep: 256 + 256 rows x 128 bytes = 64 KB each), so the loads of step k+2
-// go out while step k is multiplied.
+// LDS base + 16 l) and no registers stage them.  LDS holds NB K-steps
+// (128-deep: 256 + 256 rows x 128 bytes = 64 KB each for the largest tile, so
+// two of those; four of the 32 KB steps of a 128 x 128 tile), and the loads of
+// step k+NB go out while step k is multiplied.
 //
 // Each load instruction covers eight rows x 128 bytes: every 128-byte line it
 // touches is read whole, once.  (Four-row-per-64-byte-half layouts -- one line
@@ -58,7 +62,7 @@ struct BigCfg {
 // address bit 6 only (slot bit 2).
 __device__ __forceinline__ int dl_f(int r) { return (r >> 1) & 7; }
 
-// LDS of the direct-to-LDS kernel: two K-step buffers of operand data (weight
+// LDS of the direct-to-LDS kernel: NB K-step buffers of operand data (weight
 // rows, then token rows), then two buffers of scale words.  A scale buffer holds
 // the words of four K-steps for every row of both operands, 16 bytes per row, so
 // the scale loads touch each row once per four K-steps instead of once per step:
@@ -71,8 +75,8 @@ struct DlLds {
   static constexpr int W = 0, X = C::BN * 128;            // within a step's data
   static constexpr int SROWS = C::BN + C::BM;              // weight rows, then token rows
   static constexpr int SBUF = SROWS * 16;
-  static constexpr int SCALES = 2 * DATA;
-  static constexpr int BYTES = 2 * DATA + 2 * SBUF;
+  static constexpr int SCALES = C::NB * DATA;
+  static constexpr int BYTES = C::NB * DATA + 2 * SBUF;
   static_assert(DATA <= 65536, "tile offsets of a step within one LDS offset window");
   static_assert(BYTES <= 160 * 1024, "LDS of one CU");
 };
@@ -179,9 +183,9 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   const int base = (int)lds_addr(smem);
   // read bases per step buffer: chunk q of row i (lo, first half step); chunk
   // 2 + q is that address ^ 32, and the second half step's chunks are ^ 64
-  int aw0[2], ax0[2];
+  int aw0[C::NB], ax0[C::NB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < C::NB; ++b) {
     aw0[b] = base + b * Lds::DATA + Lds::W + wn * C::TN * 4096 + 128 * i + 16 * (q ^ fi);
     ax0[b] = base + b * Lds::DATA + Lds::X + wm * C::TM * 4096 + 128 * i + 16 * (q ^ fi);
   }
@@ -189,10 +193,10 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   const int axs = base + Lds::SCALES + (C::BN + wm * C::TM * 32 + i) * 16;
   // Fragment read r of half step H of K-step J (mod 8) of the unrolled loop: r < TN
   // is weight tile r, then token tile r - TN; each is a scale word and two 16-byte
-  // halves.  K-step J lives in step buffer J % 2 and scale buffer J / 4, scale word J % 4.
+  // halves.  K-step J lives in step buffer J % NB and scale buffer J / 4, scale word J % 4.
   auto read_tile = [&](auto r_tag, auto j_tag, auto h_tag, Frags& F) {
     constexpr int r = decltype(r_tag)::value, J = decltype(j_tag)::value, H = decltype(h_tag)::value;
-    constexpr int B = J % 2, SB = (J / 4) * Lds::SBUF + (J % 4) * 4;
+    constexpr int B = J % C::NB, SB = (J / 4) * Lds::SBUF + (J % 4) * 4;
     if constexpr (r < C::TN) {
       F.sw[r] = lds_read4<SB + r * 512>(aws);
       F.fw[r] = join8(lds_read16_xor<r * 4096, 64 * H>(aw0[B]), lds_read16_xor<r * 4096, 64 * H + 32>(aw0[B]));
@@ -210,33 +214,36 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     if (k <= C::TM) return C::TN + k - 1;                   // X0 .. X(TM-1)
     return k - C::TM;                                       // W1 .. W(TN-1)
   };
-  static_assert(C::TN == 4 && C::TM <= 4, "register ties below list the tiles by name");
+  static_assert(C::TN % 2 == 0, "weight tiles split evenly over the two halves of a half step");
   constexpr int LATE_LDS_OPS = 3 * (C::TN / 2);             // scale word + two halves per late tile
   auto shift_scales = [&](Frags& F, int a0, int a1, bool x) {
     for (int a = a0; a < a1; ++a) F.sw[a] = (int)((uint32_t)F.sw[a] >> (8 * q));
     if (x)
       for (int c = 0; c < C::TM; ++c) F.sx[c] = (int)((uint32_t)F.sx[c] >> (8 * q));
   };
+  // register ties: each placed right after the s_waitcnt that covers the reads
+  // (volatile asm statements keep their order)
+  auto tie_w = [&](Frags& F, int a0, int a1) {
+#pragma unroll
+    for (int a = a0; a < a1; ++a) asm volatile("" : "+v"(F.fw[a]), "+v"(F.sw[a]));
+  };
   auto tie_x = [&](Frags& F) {
-    if constexpr (C::TM == 4)
-      asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.fx[2]), "+v"(F.fx[3]), "+v"(F.sx[0]), "+v"(F.sx[1]),
-                   "+v"(F.sx[2]), "+v"(F.sx[3]));
-    else
-      asm volatile("" : "+v"(F.fx[0]), "+v"(F.fx[1]), "+v"(F.sx[0]), "+v"(F.sx[1]));
+#pragma unroll
+    for (int c = 0; c < C::TM; ++c) asm volatile("" : "+v"(F.fx[c]), "+v"(F.sx[c]));
   };
   // f0 of a K-step is read last (end of the previous K-step), its late weight
   // tiles last of all: wait for all but those
   auto wait_f0_early = [&](Frags& F) {
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(F.fw[0]), "+v"(F.fw[1]) : "n"(LATE_LDS_OPS));
-    asm volatile("" : "+v"(F.sw[0]), "+v"(F.sw[1]));
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(LATE_LDS_OPS));
+    tie_w(F, 0, C::TN / 2);
     tie_x(F);
     shift_scales(F, 0, C::TN / 2, true);
   };
   // everything: f0's late tiles and all of f1
   auto wait_f0_late_f1 = [&](Frags& F0, Frags& F1) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F0.fw[2]), "+v"(F0.fw[3]), "+v"(F0.sw[2]), "+v"(F0.sw[3]));
-    asm volatile("" : "+v"(F1.fw[0]), "+v"(F1.fw[1]), "+v"(F1.fw[2]), "+v"(F1.fw[3]), "+v"(F1.sw[0]), "+v"(F1.sw[1]),
-                 "+v"(F1.sw[2]), "+v"(F1.sw[3]));
+    asm volatile("s_waitcnt lgkmcnt(0)");
+    tie_w(F0, C::TN / 2, C::TN);
+    tie_w(F1, 0, C::TN);
     tie_x(F1);
     shift_scales(F0, C::TN / 2, C::TN, false);
     shift_scales(F1, 0, C::TN, true);
@@ -244,11 +251,11 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
 
   // One K-step k (J = k % 8) in four quarters of NMF MFMAs each, f0's weight tiles
   // 0 .. TN/2-1, then TN/2 .. TN-1, then f1's likewise:
-  //   A1: f0's first MFMAs; reads of all of f1 (step buffer k % 2, already visible)
+  //   A1: f0's first MFMAs; reads of all of f1 (step buffer k % NB, already visible)
   //       slotted between them.  Then every wave waits for its reads and a barrier
-  //       frees step buffer k % 2 for the loads of step k+2 (and, at k = 4s, scale
+  //       frees step buffer k % NB for the loads of step k+NB (and, at k = 4s, scale
   //       buffer (s+1) % 2, last used by steps up to 4s-1, for scale group s+1).
-  //   A2, B1, B2: the rest of the MFMAs with the L loads of step k+2 spread evenly
+  //   A2, B1, B2: the rest of the MFMAs with the L loads of step k+NB spread evenly
   //       between them (one memory pipeline per CU: loads issued in a burst queue
   //       faster than it accepts them, and a wave waiting to issue a load issues no
   //       MFMA either).
@@ -256,7 +263,7 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   //       three quarters before the previous B2 ended), and a barrier makes every
   //       wave's step k+1 visible; B2 then also reads f0 of step k+1.
   // A step has no branches: a branch would split the scheduling region and let the
-  // compiler regroup the MFMAs.  Every step issues the loads of step k+2 and, at
+  // compiler regroup the MFMAs.  Every step issues the loads of step k+NB and, at
   // k = 4s, of scale group s+1 -- switched off (zero-byte resources) where those do
   // not exist -- so the number of loads issued after step k+1's is a constant, and
   // the last step's reads fetch a buffer that is never used.
@@ -268,7 +275,7 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     constexpr int J = decltype(j_tag)::value, Q = decltype(quarter_tag)::value;   // Q: 0 = A1 .. 3 = B2
     constexpr int H = Q / 2;
     Frags& F = H == 0 ? f0 : f1;
-    const bool on = k + 2 < ksteps;
+    const bool on = k + C::NB < ksteps;
     static_for<NMF>([&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
       constexpr int a = (Q % 2) * (C::TN / 2) + m / C::TM, b = m % C::TM;
@@ -290,7 +297,7 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
         static_for<L>([&](auto d_tag) {
           constexpr int d = decltype(d_tag)::value;
           if constexpr (load_slot(d) == (Q - 1) * NMF + m)
-            issue_one(d_tag, std::integral_constant<int, J % 2>{}, k + 2, on);
+            issue_one(d_tag, std::integral_constant<int, J % C::NB>{}, k + C::NB, on);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -308,18 +315,21 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(j_tag, std::integral_constant<int, 1>{}, k);
     mfma_q(j_tag, std::integral_constant<int, 2>{}, k);
-    // loads issued after step k+1's last one: A2 and B1 of this step, and scale
-    // group s+1 when it went out at the start of A2 (k = 4s)
-    wait_vmcnt<P12 + (J % 4 == 0 ? SI : 0)>();
+    // loads issued after step k+1's last one (which went out in step k+1-NB): the
+    // loads of steps k+2 .. k+NB-1 (steps k+2-NB .. k-1), A2 and B1 of this step,
+    // and a scale group if one went out in steps k+2-NB .. k (at steps 4s)
+    wait_vmcnt<(C::NB - 2) * L + P12 + (J % 4 <= C::NB - 2 ? SI : 0)>();
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(j_tag, std::integral_constant<int, 3>{}, k);
   };
 
   issue_scales(std::integral_constant<int, 0>{}, 0, true);
-  static_for<L>([&](auto d_tag) { issue_one(d_tag, std::integral_constant<int, 0>{}, 0, true); });
-  static_for<L>([&](auto d_tag) { issue_one(d_tag, std::integral_constant<int, 1>{}, 1, 1 < ksteps); });
-  wait_vmcnt<L>();                                 // scale group 0 and step 0
+  static_for<C::NB>([&](auto b_tag) {
+    constexpr int b = decltype(b_tag)::value;
+    static_for<L>([&](auto d_tag) { issue_one(d_tag, b_tag, b, b < ksteps); });
+  });
+  wait_vmcnt<(C::NB - 1) * L>();                   // scale group 0 and step 0
   asm volatile("s_barrier" ::: "memory");
   static_for<NT>([&](auto t_tag) {
     read_tile(std::integral_constant<int, order(decltype(t_tag)::value)>{}, std::integral_constant<int, 0>{},
@@ -335,8 +345,8 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   // waited for within the step) and the switched-off loads -- which still write zeros into the step buffers that the
   // epilogue reuses -- have all landed before the barrier below.
   wait_vmcnt<0>();
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f0.fw[0]), "+v"(f0.fw[1]), "+v"(f0.fw[2]), "+v"(f0.fw[3]), "+v"(f0.sw[0]),
-               "+v"(f0.sw[1]), "+v"(f0.sw[2]), "+v"(f0.sw[3]));
+  asm volatile("s_waitcnt lgkmcnt(0)");
+  tie_w(f0, 0, C::TN);
   tie_x(f0);
 
   // Epilogue through LDS, one 32-token block at a time.
@@ -365,20 +375,20 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   }
 }
 
-// Tile configurations: 256 weight rows x 256 tokens; 128 x 256 when N is not a
-// multiple of 256 and for the last rows of tokens (below).
-using Cfg256 = BigCfg<256, 256, 2, 2>;   // 128 x 128 per wave
-using Cfg128 = BigCfg<128, 256, 1, 4>;   // 128 x 64 per wave
+// Tile configurations.  Many tokens: 256 weight rows x 256 tokens, 128 x 256 when
+// N is not a multiple of 256 and for the last rows of tokens (below); two step
+// buffers.  Fewer tokens (too few 256 x 256 tiles for 256 CUs): 128 x 128 and
+// 64 x 128 tiles with four step buffers, three steps of loads in flight.
+using Cfg256 = BigCfg<256, 256, 2, 2>;      // 128 x 128 per wave
+using Cfg128 = BigCfg<128, 256, 1, 4>;      // 128 x 64 per wave
+using Mid128 = BigCfg<128, 128, 2, 2, 4>;   // 64 x 64 per wave
+using Mid64 = BigCfg<64, 128, 1, 4, 4>;     // 64 x 32 per wave
 
-// The kernel: rows of 256 tokens [0, full_rows) as CF tiles, the remaining rows
-// as CT tiles (narrower: more of them, so a short last round of the machine is
-// spread over more CUs).  Each output element is one whole-K accumulation in
-// both, with the same operand bytes in the same order, so the tile shape never
-// changes a result.
 template <class CF, class CT, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dl_gemm_kernel(GemmArgs p, int G, int full_rows, int rows) {
-  static_assert(CF::BM == 256 && CT::BM == 256, "rows of 256 tokens");
+  static_assert(CF::BM == CT::BM, "rows of BM tokens");
+  constexpr int BM = CF::BM;
   constexpr int BYTES = DlLds<CF>::BYTES > DlLds<CT>::BYTES ? DlLds<CF>::BYTES : DlLds<CT>::BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[BYTES];
   const int nf = (int)(p.N / CF::BN), ntl = (int)(p.N / CT::BN);
@@ -386,12 +396,12 @@ void dl_gemm_kernel(GemmArgs p, int G, int full_rows, int rows) {
   if ((int)blockIdx.x < F) {
     const int wi = xcd_work_index((int)blockIdx.x, F);
     const int nt = wi % nf, rest = wi / nf, mt = rest % full_rows, g = rest / full_rows;
-    dl_tile<CF, OUT>(p, smem, g, (int64_t)nt * CF::BN, (int64_t)mt * 256);
+    dl_tile<CF, OUT>(p, smem, g, (int64_t)nt * CF::BN, (int64_t)mt * BM);
   } else {
     const int tr = rows - full_rows;
     const int wi = xcd_work_index((int)blockIdx.x - F, G * ntl * tr);
     const int nt = wi % ntl, rest = wi / ntl, mt = full_rows + rest % tr, g = rest / tr;
-    dl_tile<CT, OUT>(p, smem, g, (int64_t)nt * CT::BN, (int64_t)mt * 256);
+    dl_tile<CT, OUT>(p, smem, g, (int64_t)nt * CT::BN, (int64_t)mt * BM);
   }
 }
 
@@ -410,6 +420,7 @@ static hipError_t dispatch_out(const GemmArgs& p, const GemmPlan& plan, int64_t 
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& p, const GemmPlan& plan, int64_t G, int out, hipStream_t stream) {
+  if (plan.tile_cfg == TILE_MID) return dispatch_out<Mid128, Mid64>(p, plan, G, out, stream);   // N % 128 == 0
   if (p.N % 256 == 0) return dispatch_out<Cfg256, Cfg128>(p, plan, G, out, stream);
   return dispatch_out<Cfg128, Cfg128>(p, plan, G, out, stream);
 }
@@ -425,6 +436,7 @@ constexpr int64_t kSkinnyMaxSteps = 32;       // 128-deep steps per split (the s
 // takes in twice the activation bytes.  BF16 activations are quantized into the
 // workspace first.
 constexpr int64_t kWholeKMaxSteps = 64;
+constexpr int64_t kSkinnyTileMinTokens = 128;
 
 static bool whole_k_fits(int64_t M, int64_t G, int64_t N, int64_t K) {
   if (N % 32 != 0 || K / 128 > kWholeKMaxSteps) return false;
@@ -436,7 +448,7 @@ static bool whole_k_fits(int64_t M, int64_t G, int64_t N, int64_t K) {
 // calls share a workspace.
 constexpr int64_t kCounterBytes = 65536;
 // Many-token tiles: one resident workgroup per CU on MI355X's 256 CUs; a
-// 128 x 256 tile takes about this fraction of a 256 x 256 tile's time.
+// half-width tile takes about this fraction of a wide tile's time.
 constexpr int64_t kTileCUs = 256;
 constexpr double kNarrowTileCost = 0.65;
 
@@ -477,17 +489,34 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
   const int mt = M <= 32 ? 1 : 2;
   const int64_t chunks = (M + 63) / 64;
   const int64_t tiles = G * (N / 64) * chunks;
-  pl.skinny = M <= kSkinnyMaxTokens && tiles * 8 <= kCounterBytes;     // one 64-bit counter per tile
+  // The few-token kernels up to 128 tokens (one row of 128-token tiles leaves wo_b
+  // 80 workgroups); from 129 to 256 tokens only while the grid of 64 x 128 tiles
+  // would stay under a quarter of the CUs.  Measured, o_proj chain with the
+  // einsum and wo_b on 128 x 128 tiles against the split-K kernel: 50.4 / 53.9 /
+  // 57.7 us against 52.3 / 53.9 / 55.6 at 65 / 96 / 128 tokens, 55.2 / 57.0
+  // against 69.2 / 71.6 at 160 / 192.
+  const bool few_tiles = G * (N / 64) * ((M + 127) / 128) < kTileCUs / 4;
+  pl.skinny = (M <= kSkinnyTileMinTokens || (M <= kSkinnyMaxTokens && few_tiles)) &&
+              tiles * 8 <= kCounterBytes;     // one 64-bit counter per tile
   if (!pl.skinny) {
-    const int64_t rows = (M + 255) / 256;
+    // Tile family: 128-token rows of 128 x 128 / 64 x 128 tiles while the 256 x 256
+    // grid would cover at most a quarter of the CUs, else 256-token rows of
+    // 256 x 256 / 128 x 256 tiles.  Measured (einsum 8 x 4096 -> 1024; wo_b
+    // 8192 -> 5120): the smaller tiles are 1.25-1.8x faster up to 512 / 768 tokens
+    // (64 / 60 big tiles) and 0.63-0.87x from 640 / 1024 tokens (96 / 80) on.
+    const int64_t big_tiles = G * (N / 256 > 0 ? N / 256 : 1) * ((M + 255) / 256);
+    const bool mid = big_tiles <= kTileCUs / 4;
+    pl.tile_cfg = mid ? TILE_MID : TILE_BIG;
+    const int64_t bm = mid ? 128 : 256, bn = mid ? 128 : 256;
+    const int64_t rows = (M + bm - 1) / bm;
     pl.rows = (int)rows;
     pl.full_rows = (int)rows;
-    if (N % 256 == 0) {
-      // How many rows of 256 tokens get 256-wide tiles: the one that finishes
-      // first when the tiles are dealt in order to kTileCUs CUs, one each, a
-      // 128-wide tile costing kNarrowTileCost of a 256-wide one (fewest narrow
-      // tiles among equal estimates).  Many rounds leave little to gain: skip.
-      const int64_t per_row = G * (N / 256);
+    if (N % bn == 0) {
+      // How many rows of tokens get wide tiles: the split that finishes first
+      // when the tiles are dealt in order to kTileCUs CUs, one each, a half-width
+      // tile costing kNarrowTileCost of a wide one (fewest narrow tiles among
+      // equal estimates).  Many rounds leave little to gain: skip.
+      const int64_t per_row = G * (N / bn);
       if (per_row * rows < 4 * kTileCUs) {
         double best = 1e30;
         for (int64_t r = rows; r >= 0; --r) {
@@ -500,7 +529,8 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
       }
       pl.workgroups = per_row * pl.full_rows + 2 * per_row * (rows - pl.full_rows);
     } else {
-      pl.workgroups = G * (N / 128) * rows;
+      pl.full_rows = 0;
+      pl.workgroups = G * (N / (bn / 2)) * rows;
     }
     if (x_bf16 && M > 0) stage_bf16(pl, M, G * K);
     return pl;

@@ -34,6 +34,8 @@ struct GemmArgs {
   int splitk_mode;        // how split-K partials are combined (SplitKMode)
 };
 
+enum TileCfg { TILE_BIG = 0, TILE_MID = 1 };
+
 // Kernel choice and scratch needs of one GEMM launch: a pure function of
 // (M, G, N, K, activation kind).  Workspace layout, each part 256-byte aligned:
 // split-K arrival counters, split-K fp32 partial tiles, then -- BF16 activations
@@ -48,8 +50,10 @@ struct GemmPlan {
   int n_tiles;            // weight tiles per group (skinny: 64 rows; whole_k: 32 rows)
   int splits;             // K splits (skinny)
   int64_t workgroups;
-  int full_rows;          // many tokens: rows of 256 tokens done as 256-wide weight tiles ...
-  int rows;               //   ... of all ceil(M / 256) rows; the rest as 128-wide tiles
+  int tile_cfg;           // many tokens: TILE_BIG (rows of 256 tokens: 256- and 128-wide weight tiles)
+                          //   or TILE_MID (rows of 128 tokens: 128- and 64-wide weight tiles)
+  int full_rows;          // many tokens: rows of tokens done as wide weight tiles ...
+  int rows;               //   ... of all ceil(M / row height) rows; the rest as half-width tiles
   int64_t counter_bytes;  // leading part of the workspace: one 64-bit counter per (tile, chunk)
   int64_t stage_offset;   // BF16 activations, many tokens: codes [M][G*K] at this offset
   int64_t stage_sf_offset;//   and packed scales [M][G*K/128] at this one (0 when unused)

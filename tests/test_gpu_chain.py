@@ -302,12 +302,18 @@ def test_decode_shapes_bitexact(lib, kind, M, G, N, K):
 @pytest.mark.parametrize("kind,M,G,N,K", [("gemm", 65, 1, 5120, 8192), ("gemm", 300, 1, 5120, 2048),
                                           ("gemm", 512, 1, 2560, 4096), ("gemm", 300, 1, 384, 1024),
                                           ("einsum", 129, 8, 1024, 4096), ("einsum", 256, 4, 1024, 2048),
-                                          ("einsum", 700, 2, 1024, 1024), ("einsum", 97, 3, 384, 1152)])
+                                          ("einsum", 700, 2, 1024, 1024), ("einsum", 97, 3, 384, 1152),
+                                          ("gemm", 200, 1, 5120, 8192), ("gemm", 767, 1, 5120, 1152),
+                                          ("einsum", 385, 8, 1024, 4096), ("gemm", 1100, 1, 640, 2048),
+                                          ("einsum", 130, 5, 640, 640), ("gemm", 1100, 1, 5120, 1152),
+                                          ("gemm", 130, 1, 256, 4096)])
 def test_mid_range_shapes_bitexact(lib, kind, M, G, N, K):
-    """65 to about 1000 tokens (split-K streaming kernel up to 256 tokens, tiles of 256 tokens above; 256- and
-    128-wide weight tiles, ragged token counts, K ranges that are not multiples of four steps): bit-exact
-    against the oracle in the exact regime in each combine mode, for every output form; counters return to
-    zero."""
+    """65 to about 1000 tokens: the split-K streaming kernel (up to 128 tokens, and up to 256 on small grids),
+    128-token rows
+    of 128- and 64-wide weight tiles (while the 256 x 256 grid would cover at most a quarter of the CUs),
+    256-token rows of 256- and 128-wide tiles above; ragged token counts, K ranges that are not multiples of
+    four steps, weight counts that are odd multiples of 128: bit-exact against the oracle in the exact regime
+    in each combine mode, for every output form; counters return to zero."""
     _modes_bitexact(lib, kind, M, G, N, K, 9300 + M + N)
 
 
