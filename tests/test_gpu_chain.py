@@ -85,6 +85,40 @@ def test_mixed_tile_shapes_bitexact(lib, kind, M, G, N, K):
     assert np.array_equal(to_np(d), ref)
 
 
+@pytest.mark.parametrize("kind,M_small,M_big,G,N,K", [("einsum", 512, 1024, 8, 1024, 4096),
+                                                      ("gemm", 768, 1024, 1, 5120, 8192),
+                                                      ("gemm", 300, 2000, 1, 2560, 1024)])
+def test_tile_families_give_identical_bits(lib, kind, M_small, M_big, G, N, K):
+    """Random operands, outside the exact regime: the same token rows computed in a launch that takes the
+    128 x 128 tile family (M_small) and in one that takes the 256 x 256 family (M_big, with 128 x 256 tiles
+    for its last rows) are bit-identical -- every output element is one whole-K accumulation of the same
+    bytes in the same order whatever the tile shape."""
+    rng = np.random.default_rng(11000 + M_big)
+
+    def random_mxfp8(rows, cols):
+        q = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] ^= 1                                  # no NaN codes
+        sb = rng.integers(120, 131, size=(rows, cols // 32)).astype(np.uint8)
+        return q, mx.pack_scales(sb)
+
+    aq, asf = random_mxfp8(M_big, G * K)
+    wq, wsf = random_mxfp8(G * N, K)
+    outs = []
+    for M in (M_small, M_big):
+        a_t, asf_t = u8_to_dev(aq[:M]), i32_to_dev(asf[:M])
+        if kind == "gemm":
+            outs.append(to_np(lib.fp8_gemm_nt(a_t, asf_t, u8_to_dev(wq), i32_to_dev(wsf))))
+        else:
+            z_q, z_sf, z_b = lib.grouped_fp8_einsum(a_t, asf_t, u8_to_dev(wq.reshape(G, N, K)),
+                                                    i32_to_dev(wsf.reshape(G, N, K // 128)), out="both")
+            outs.append((to_np(z_q), to_np(z_sf), to_np(z_b)))
+    if kind == "gemm":
+        assert np.array_equal(outs[0], outs[1][:M_small])
+    else:
+        for small, big in zip(outs[0], outs[1]):
+            assert np.array_equal(small, big[:M_small])
+
+
 @pytest.mark.parametrize("M", [1, 7, 12, 32])
 @pytest.mark.parametrize("kind,G,N,K", [("gemm", 1, 4096, 8192), ("gemm", 1, 5120, 384), ("einsum", 8, 512, 256),
                                         ("einsum", 4, 1024, 1152)])
