@@ -340,7 +340,12 @@ def test_decode_shapes_bitexact(lib, kind, M, G, N, K):
                                           ("gemm", 200, 1, 5120, 8192), ("gemm", 767, 1, 5120, 1152),
                                           ("einsum", 385, 8, 1024, 4096), ("gemm", 1100, 1, 640, 2048),
                                           ("einsum", 130, 5, 640, 640), ("gemm", 1100, 1, 5120, 1152),
-                                          ("gemm", 130, 1, 256, 4096)])
+                                          ("gemm", 130, 1, 256, 4096),
+                                          # either side of each switch of the plan on the o_proj shapes:
+                                          # split-K kernel | 128 x 128 tiles | 256 x 256 tiles
+                                          ("gemm", 128, 1, 5120, 8192), ("gemm", 129, 1, 5120, 8192),
+                                          ("einsum", 512, 8, 1024, 4096), ("einsum", 513, 8, 1024, 4096),
+                                          ("gemm", 768, 1, 5120, 8192), ("gemm", 769, 1, 5120, 8192)])
 def test_mid_range_shapes_bitexact(lib, kind, M, G, N, K):
     """65 to about 1000 tokens: the split-K streaming kernel (up to 128 tokens, and up to 256 on small grids),
     128-token rows
