@@ -115,7 +115,27 @@ def cpu_baseline(cfg_name, inp, budget_s=12.0):
     return {"value": tflops, "unit": "TFLOP/s", "cores": threads_used(), "kind": "oracle",
             "sample": f"{cfg_name}: first {rows} token rows, whole chain incl. weight dequantization, "
                       f"{reps} repetitions in {el:.1f} s ({el / reps * 1e6:.0f} us/call)",
-            "host_cpu": cpu, "host_threads_visible": len(os.sched_getaffinity(0))}
+            "host_cpu": cpu, "host_threads_visible": len(os.sched_getaffinity(0)),
+            "scalar_quantize": scalar_quantize_timing()}
+
+
+def scalar_quantize_timing():
+    """The oracle's scalar (pure-Python, exact-rational) quantizer, one thread, labelled "scalar": the tiny
+    configuration's x and the quantize-sweep rows at M = 1 and 7 (larger M take minutes)."""
+    import synth_inputs as si
+    from oracle import mxfp8_ref as mx
+
+    cases = {}
+    tiny = si.CHAIN_CONFIGS["tiny"]
+    inputs = {"tiny x [4, 512]": si.chain_inputs(tiny.shape, tiny.seed, tiny.outlier_rate)["x"]}
+    for M in (1, 7):
+        inputs[f"quantize sweep [{M}, 7168]"] = si.quant_sweep_input(M)
+    for name, x in inputs.items():
+        t0 = time.perf_counter()
+        mx.quantize_scalar(x)
+        el = time.perf_counter() - t0
+        cases[name] = {"us_per_call": el * 1e6, "ns_per_element": el * 1e9 / x.size}
+    return {"kind": "scalar", "threads": 1, "cases": cases}
 
 
 def copy_calibration(torch, mib):
