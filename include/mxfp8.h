@@ -35,9 +35,10 @@
  *   - Outputs must not overlap inputs or each other (MXFP8_ERR_ALIAS).
  *   - Workspace: the GEMM entry points may need device scratch -- split-K
  *     partial sums, and, for BF16 activations that go to a kernel reading E4M3
- *     (more than 256 rows, or at most 32 rows when each workgroup can take the
- *     whole K range), the activations quantized to MXFP8 (the library quantizes
- *     BF16 input with mxfp8_quantize first).  The matching
+ *     (the tile kernels: more than 128 rows on large grids, more than 256 on
+ *     small ones; the whole-K kernel: 17 to 64 rows, or fewer at K depths other
+ *     than 32 or 64 steps), the activations quantized to MXFP8 (the library
+ *     quantizes BF16 input with mxfp8_quantize first).  The matching
  *     *_workspace_size(kind, shape) call gives the bytes (0 = none needed,
  *     pointer may be NULL).  The caller owns it, zero-fills it once before first
  *     use (256-byte aligned).  Split-K calls keep arrival counters in its first
