@@ -85,6 +85,41 @@ def test_mixed_tile_shapes_bitexact(lib, kind, M, G, N, K):
     assert np.array_equal(to_np(d), ref)
 
 
+def _random_shapes(n, seed, m_range, n_steps):
+    """Seeded shapes around the tile kernels' plan: tokens in m_range, 1-4 groups, weight rows in 128-steps
+    from n_steps, 1-12 K-steps (fewer steps than step buffers included), einsum and GEMM."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        kind = "einsum" if rng.random() < 0.5 else "gemm"
+        M = int(rng.integers(*m_range))
+        G = int(rng.integers(1, 5)) if kind == "einsum" else 1
+        N = 128 * int(rng.integers(*n_steps))
+        K = 128 * int(rng.integers(1, 13))
+        out.append((kind, M, G, N, K))
+    return out
+
+
+@pytest.mark.parametrize("kind,M,G,N,K", _random_shapes(16, 20261202, (129, 1501), (1, 13)) +
+                         _random_shapes(8, 20261203, (700, 3001), (8, 41)))
+def test_random_tile_shapes_bitexact(lib, kind, M, G, N, K):
+    """Seeded random shapes through the tile kernels (both families, wide and half-width tiles, ragged
+    token rows, short K ranges): bit-exact against the oracle in the exact regime, every output form."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    aq, asf = exact_operands(rng, M, G * K)
+    wq, wsf = exact_operands(rng, G * N, K)
+    if kind == "gemm":
+        d = lib.fp8_gemm_nt(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq), i32_to_dev(wsf))
+        assert np.array_equal(to_np(d), mx.bf16_round(cr.gemm_nt(aq, asf, wq, wsf)))
+        return
+    ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
+    oq, osf = mx.quantize(ref)
+    z_q, z_sf, z_b = lib.grouped_fp8_einsum(u8_to_dev(aq), i32_to_dev(asf), u8_to_dev(wq.reshape(G, N, K)),
+                                            i32_to_dev(wsf.reshape(G, N, K // 128)), out="both")
+    assert np.array_equal(to_np(z_b), ref)
+    assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf)
+
+
 @pytest.mark.parametrize("kind,M_small,M_big,G,N,K", [("einsum", 512, 1024, 8, 1024, 4096),
                                                       ("gemm", 768, 1024, 1, 5120, 8192),
                                                       ("gemm", 300, 2000, 1, 2560, 1024)])
