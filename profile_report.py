@@ -15,6 +15,10 @@
     python profile_report.py pmc P.csv [--title T] [--command C]
         Mean of each collected counter per dispatch, for each launch of the chain.
 
+    python profile_report.py chain DB.db [--title T] [--command C]
+        µs per chain call from the kernel trace: quantize start to gemm end of each
+        consecutive quantize -> einsum -> gemm triple, with the launches and gaps.
+
 Kernels are told apart by name and output mode (the streaming kernel's second
 template argument, the whole-K kernel's first, the tile kernel's last: 1 = BF16
 out: fp8_gemm_nt, 2 = MXFP8 out: grouped_fp8_einsum); the quantize kernel is
@@ -187,6 +191,45 @@ def cmd_pmc(a):
         print(f"| {role} | {k[1]} | {n} | " + " | ".join(cells) + " |")
 
 
+def cmd_chain(a):
+    """µs per chain call from kernel-trace timestamps: each quantize -> einsum -> gemm triple of consecutive
+    dispatches (the headline chain), from the quantize's start to the gemm's end; plus each launch's
+    duration and the gaps between them."""
+    import statistics
+
+    db = sqlite3.connect(a.db)
+    rows = db.execute("select name, start, end, grid_x from kernels order by start").fetchall()
+    seq = [(chain_role(n), s, e, g) for n, s, e, g in rows]
+    # the chain's own quantize grid: the most frequent quantize grid
+    qgrids = collections.Counter(g for r, _, _, g in seq if r == "quantize")
+    if not qgrids:
+        raise SystemExit("no quantize dispatch in the trace")
+    qgrid = qgrids.most_common(1)[0][0]
+    spans, parts = [], collections.defaultdict(list)
+    for i in range(len(seq) - 2):
+        q, e, g = seq[i], seq[i + 1], seq[i + 2]
+        if q[0] == "quantize" and q[3] == qgrid and e[0] == "einsum" and g[0] == "gemm":
+            spans.append((g[2] - q[1]) / 1e3)
+            parts["quantize"].append((q[2] - q[1]) / 1e3)
+            parts["gap quantize -> einsum"].append((e[1] - q[2]) / 1e3)
+            parts["einsum"].append((e[2] - e[1]) / 1e3)
+            parts["gap einsum -> gemm"].append((g[1] - e[2]) / 1e3)
+            parts["gemm"].append((g[2] - g[1]) / 1e3)
+    if not spans:
+        raise SystemExit("no quantize -> einsum -> gemm sequence in the trace")
+    if a.title:
+        print(f"# {a.title}\n")
+    if a.command:
+        print("Command (from the repository root, one MI355X):\n\n    " + a.command + "\n")
+    q = statistics.quantiles(spans, n=10)
+    print(f"{len(spans)} chain calls (quantize start -> gemm end): median {statistics.median(spans):.2f} µs, "
+          f"min {min(spans):.2f}, 10th percentile {q[0]:.2f}, 90th percentile {q[-1]:.2f}.\n")
+    print("| part | median µs | min µs |")
+    print("|---|---|---|")
+    for k, v in parts.items():
+        print(f"| {k} | {statistics.median(v):.2f} | {min(v):.2f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -206,8 +249,12 @@ def main():
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command", action="append")
+    c = sub.add_parser("chain")
+    c.add_argument("db")
+    c.add_argument("--title", default="")
+    c.add_argument("--command", default="")
     a = ap.parse_args()
-    {"kernels": cmd_kernels, "traffic": cmd_traffic, "pmc": cmd_pmc}[a.cmd](a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "pmc": cmd_pmc, "chain": cmd_chain}[a.cmd](a)
 
 
 if __name__ == "__main__":
