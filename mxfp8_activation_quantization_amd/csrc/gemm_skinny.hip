@@ -453,7 +453,7 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
 }
 
 // ---------------------------------------------------------------------------
-// At most 64 tokens: whole K per workgroup, no split.
+// At most 128 tokens: whole K per workgroup, no split.
 //
 // With few tokens the activation bytes per weight row are small, so a workgroup
 // can own 32 weight rows over the whole K range and the grid still covers most of
@@ -461,13 +461,14 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
 // workgroup.  Up to 32 tokens (one token tile) the four waves take the 128-deep
 // steps in turn (step j: wave j % 4), each into its own accumulator; with 33 to 64
 // tokens (two token tiles) waves 2 tt and 2 tt + 1 take the even and odd steps of
+// token tile tt; with 65 to 128 (four token tiles) wave tt takes every step of
 // token tile tt.  At the end the partial tiles of a token tile are added in wave
 // order through LDS and the first wave of the tile stores it.
 //
 // Ring: kGvStages stages of SS steps (SS = the waves per token tile, so every
 // wave multiplies one step of every stage); per step 32 weight rows and 8 XG token
-// rows x 128 bytes (XG = 1, 2, 4 or 8 groups of 8 token rows, the fewest that hold
-// M), the slot layout of the streaming kernel above.  The ring is shallow on
+// rows x 128 bytes (XG = 1, 2, 4, 8 or 16 groups of 8 token rows, the fewest that
+// hold M), the slot layout of the streaming kernel above.  The ring is shallow on
 // purpose: with every CU streaming at once, deeper rings (8 to 12 stages of two
 // steps were measured) finished later, and four stages of four steps (48 KB of
 // weights in flight per CU) were fastest at both wo_a and wo_b shapes.  Token
@@ -479,10 +480,11 @@ constexpr int kGvStages = 4;
 
 template <int XG>
 struct GvCfg {
-  static constexpr int MT = XG > 4 ? 2 : 1;       // token tiles
+  static constexpr int MT = XG > 8 ? 4 : (XG > 4 ? 2 : 1);   // token tiles
   static constexpr int SS = 4 / MT;               // steps per stage = waves per token tile
   static constexpr int XR = 8 * XG;               // token rows in a stage
-  static constexpr int XI = XG > 4 ? 2 : 1;       // activation loads per wave and step, at most
+  static constexpr int XI = MT;                   // activation loads per wave and step, at most
+  static_assert(XG <= 16 && XR <= 32 * MT, "token rows of the token tiles");
 };
 
 template <int XG>
@@ -557,7 +559,9 @@ void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
     const int r = 8 * (wave + 4 * u) + lr;
     vx[u] = r * ldx + (lc ^ g8(r)) * 16;
   }
-  const int nx = (8 * wave < m_rows ? 1 : 0) + (C::XI > 1 && 8 * (wave + 4) < m_rows ? 1 : 0);
+  int nx = 0;                                       // activation loads of this wave and step
+#pragma unroll
+  for (int u = 0; u < C::XI; ++u) nx += 8 * (wave + 4 * u) < m_rows ? 1 : 0;
 
   // scale tables: instruction n covers rows 4n .. 4n+3; lane l loads chunk l % 16 of row
   // 4n + l / 16 into position (l % 16) ^ (row % 16).  The whole offset is in the per-lane
@@ -588,7 +592,7 @@ void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
     }
   };
 
-  const int xi = C::MT == 2 ? 32 * tt + i : (i & (XR - 1));   // the token row this lane reads
+  const int xi = C::MT >= 2 ? 32 * tt + i : (i & (XR - 1));   // the token row this lane reads
   v16f acc = zero16();
   auto loop = [&](auto l_tag) {
     constexpr int L = decltype(l_tag)::value;       // this wave's loads per stage
@@ -609,9 +613,10 @@ void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
       }
     }
   };
-  if (nx == 0) loop(std::integral_constant<int, SS>{});
-  else if (C::XI == 1 || nx == 1) loop(std::integral_constant<int, 2 * SS>{});
-  else loop(std::integral_constant<int, 3 * SS>{});
+  static_for<C::XI + 1>([&](auto n_tag) {
+    constexpr int n = decltype(n_tag)::value;
+    if (nx == n) loop(std::integral_constant<int, (1 + n) * SS>{});
+  });
 
   // the partial tiles of each token tile, added in wave order
   __syncthreads();
@@ -836,6 +841,7 @@ static hipError_t launch_whole_k(const GemmArgs& p, const GemmPlan& plan, int64_
   if (p.M <= 16) return launch_whole_k_xg<OUT, 2>(p, plan, G, stream);
   if (p.M <= 32) return launch_whole_k_xg<OUT, 4>(p, plan, G, stream);
   if (p.M <= 64) return launch_whole_k_xg<OUT, 8>(p, plan, G, stream);
+  if (p.M <= 128) return launch_whole_k_xg<OUT, 16>(p, plan, G, stream);
   return hipErrorInvalidValue;
 }
 

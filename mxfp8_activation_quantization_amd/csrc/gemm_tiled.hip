@@ -451,16 +451,22 @@ constexpr int64_t kSkinnyTargetWorkgroups = 256;
 constexpr int64_t kSkinnyMaxSteps = 32;       // 128-deep steps per split (the streaming kernel's scale tables)
 // Few tokens: a workgroup owns 32 weight rows over the whole K range (no split)
 // when K fits its scale tables and the grid is wide enough -- at least 128
-// workgroups up to 32 tokens, 256 (every CU) up to 64, where each workgroup also
-// takes in twice the activation bytes.  BF16 activations are quantized into the
-// workspace first.
+// workgroups up to 32 tokens, 256 (every CU) from 33 to 64, where each workgroup
+// also takes in twice the activation bytes (wo_b's 160 workgroups stay on the
+// split-K kernel there: 15.7-16.0 us against 18.6-18.9), and 128 again from 65
+// to 128 tokens, where the split-K kernel streams every weight row once per 64
+// tokens (o_proj chain: 39.9 / 42.8 / 47.4 us against 52.3 / 53.4 / 55.8 at
+// 65 / 96 / 128 tokens, alternated on one box).  BF16 activations are quantized
+// into the workspace first, except where the whole-K kernel quantizes them itself.
 constexpr int64_t kWholeKMaxSteps = 64;
 constexpr int64_t kSkinnyTileMinTokens = 128;
 
 static bool whole_k_fits(int64_t M, int64_t G, int64_t N, int64_t K) {
   if (N % 32 != 0 || K / 128 > kWholeKMaxSteps) return false;
   const int64_t workgroups = G * (N / 32);
-  return M <= 32 ? workgroups >= 128 : (M <= 64 && workgroups >= 256);
+  if (M <= 32) return workgroups >= 128;
+  if (M <= 64) return workgroups >= 256;
+  return M <= 128 && workgroups >= 128;
 }
 // The workspace always starts with this many bytes of arrival counters, whatever the
 // shape, so one shape's partial tiles never land on another shape's counters when
@@ -512,8 +518,9 @@ GemmPlan plan_gemm(int64_t M, int64_t G, int64_t N, int64_t K, bool x_bf16) {
   // 80 workgroups); from 129 to 256 tokens only while the grid of 64 x 128 tiles
   // would stay under a quarter of the CUs.  Measured, o_proj chain with the
   // einsum and wo_b on 128 x 128 tiles against the split-K kernel: 50.4 / 53.9 /
-  // 57.7 us against 52.3 / 53.9 / 55.6 at 65 / 96 / 128 tokens, 55.2 / 57.0
-  // against 69.2 / 71.6 at 160 / 192.
+  // 57.7 us against 52.3 / 53.9 / 55.6 at 65 / 96 / 128 tokens (the whole-K
+  // kernel now takes those: 39.9 / 42.8 / 47.4), 55.2 / 57.0 against 69.2 / 71.6
+  // at 160 / 192.
   const bool few_tiles = G * (N / 64) * ((M + 127) / 128) < kTileCUs / 4;
   pl.skinny = (M <= kSkinnyTileMinTokens || (M <= kSkinnyMaxTokens && few_tiles)) &&
               tiles * 8 <= kCounterBytes;     // one 64-bit counter per tile

@@ -212,6 +212,10 @@ def test_workspace_sizes():
     assert LIB.grouped_fp8_einsum_workspace_size(BF, 7, 8, 4096, 1024) == 0
     assert LIB.grouped_fp8_einsum_workspace_size(BF, 16, 8, 4096, 1024) == 0
     assert LIB.grouped_fp8_einsum_workspace_size(BF, 17, 8, 4096, 1024) == 65536 + 17 * 32768 + 17 * 1024
+    # 65-128 tokens on >= 128 workgroups: whole K, E4M3 activations need nothing, BF16 ones are staged
+    assert LIB.fp8_gemm_nt_workspace_size(Q, 128, 5120, 8192) == 0
+    assert LIB.grouped_fp8_einsum_workspace_size(Q, 65, 8, 4096, 1024) == 0
+    assert LIB.fp8_gemm_nt_workspace_size(BF, 100, 5120, 8192) == 65536 + 100 * 8192 + 100 * 8192 // 32
     assert LIB.fp8_gemm_nt_workspace_size(BF, 16, 4096, 6144) == 65536 + 16 * 6144 + 16 * 6144 // 32   # 48 steps
     # too narrow for the machine (64 workgroups) or K past the scale tables: split K as before
     assert LIB.fp8_gemm_nt_workspace_size(Q, 8, 2048, 8192) > 0

@@ -200,6 +200,16 @@ def test_whole_k_two_token_tiles_bitexact(lib, kind, M, G, N, K):
     assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf)
 
 
+@pytest.mark.parametrize("M", [65, 97, 128])
+@pytest.mark.parametrize("kind,G,N,K", [("gemm", 1, 5120, 8192), ("gemm", 1, 4096, 384), ("einsum", 8, 1024, 4096),
+                                        ("einsum", 4, 1024, 1152)])
+def test_whole_k_four_token_tiles_bitexact(lib, kind, M, G, N, K):
+    """65 to 128 tokens on a grid of at least 128 workgroups: whole K per workgroup with four token tiles, one
+    wave each over every step; token rows past M in the last tile are neither loaded nor stored (M = 65, 97).
+    Bit-exact in the exact regime, every output form, no workspace."""
+    test_whole_k_two_token_tiles_bitexact(lib, kind, M, G, N, K)
+
+
 @pytest.mark.parametrize("M,G,K,N", [(4, 2, 256, 128), (45, 3, 512, 256), (96, 8, 128, 128), (3, 2, 1152, 128),
                                      (64, 2, 4096, 256), (600, 2, 512, 512), (257, 3, 256, 128),
                                      (520, 2, 1024, 384)])
