@@ -680,3 +680,44 @@ def test_shared_workspace_across_shapes(lib):
             assert np.array_equal(to_np(d), mx.bf16_round(cr.gemm_nt(zq, zsf, bq, bsf))), (rep, M)
     torch.cuda.synchronize()
     assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("M,mode", [(1, "x_fused"), (8, "x_fused"), (24, "chain"), (64, "chain"), (64, "unfused"),
+                                    (128, "chain"), (300, "chain")])
+def test_graph_replays_equal_eager(lib, M, mode):
+    """The chain captured in a HIP graph on its own stream, as the benchmark times it, gives the eager result
+    on every replay: three replays with eager chain calls on other inputs and host synchronizations between
+    them, then a replay after new contents are copied into the captured input.  The token counts take every
+    kernel of the path (load-path quantization, whole-K, split-K with its arrival counters, tiles); the
+    split-K counters must be back at zero after the replays for the next replay to be exact."""
+    c = get_case("ragged", lib)
+    args = (c.wa_q, c.wa_sf, c.wb_q, c.wb_sf)
+    x_static = c.x[:M].clone()
+    other = torch.flip(c.x, [0])[:M].contiguous()
+    eager = lib.o_proj_chain(x_static, *args, mode=mode)
+    eager_other = lib.o_proj_chain(other, *args, mode=mode)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lib.o_proj_chain(x_static, *args, mode=mode, stream=s)       # the stream's workspace, before capture
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out_static = lib.o_proj_chain(x_static, *args, mode=mode, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out_static.fill_(7.0)
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_static, eager), (M, mode, rep)
+        assert torch.equal(lib.o_proj_chain(other, *args, mode=mode), eager_other), (M, mode, rep)
+        torch.cuda.synchronize()
+    x_static.copy_(other)
+    with torch.cuda.stream(s):
+        g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out_static, eager_other), (M, mode)
+    from mxfp8_activation_quantization_amd import binding as B
+    for ws in B._workspaces.values():
+        assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
