@@ -110,8 +110,10 @@ def _rows(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 # Split-K scratch: one zero-filled buffer per (device, stream), grown on demand.  The
 # kernels leave its counters at zero, so a buffer is reusable by later calls on
-# the same stream (stream order serializes them).
+# the same stream (stream order serializes them).  An outgrown buffer is kept, not
+# freed: a graph captured earlier holds its device address and replays into it.
 _workspaces: dict = {}
+_outgrown: list = []
 
 
 def workspace_for(nbytes: int, device: torch.device, stream_ptr: int) -> torch.Tensor | None:
@@ -120,6 +122,8 @@ def workspace_for(nbytes: int, device: torch.device, stream_ptr: int) -> torch.T
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_ptr)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _outgrown.append(ws)
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws

@@ -721,3 +721,39 @@ def test_graph_replays_equal_eager(lib, M, mode):
     from mxfp8_activation_quantization_amd import binding as B
     for ws in B._workspaces.values():
         assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
+def test_graph_survives_workspace_growth(lib):
+    """A chain captured at 64 tokens (split-K wo_b: counters and partials in the stream's workspace) still
+    replays to the eager result after a larger call on the same stream has grown that stream's workspace and
+    other allocations have been made: the outgrown workspace the graph writes into stays allocated."""
+    from mxfp8_activation_quantization_amd import binding as B
+    c = get_case("ragged", lib)
+    args = (c.wa_q, c.wa_sf, c.wb_q, c.wb_sf)
+    x_static = c.x[:64].clone()
+    eager = lib.o_proj_chain(x_static, *args)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lib.o_proj_chain(x_static, *args, stream=s)
+    s.synchronize()
+    key = (dev().index or 0, s.cuda_stream)
+    ws_before = B._workspaces[key]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out_static = lib.o_proj_chain(x_static, *args, stream=s)
+    torch.cuda.synchronize()
+    # a BF16 GEMM with many tokens stages its activations in the workspace: more bytes than split-K needs
+    big = torch.randn(2048, 8192, device=dev()).to(torch.bfloat16)
+    with torch.cuda.stream(s):
+        lib.fp8_gemm_nt(big, None, c.wb_q, c.wb_sf, stream=s)
+    s.synchronize()
+    assert B._workspaces[key].data_ptr() != ws_before.data_ptr()     # the workspace did grow
+    junk = [torch.full((1 << 20,), 0x7F, dtype=torch.uint8, device=dev()) for _ in range(16)]
+    for rep in range(2):
+        out_static.fill_(7.0)
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_static, eager), rep
+    assert all(bool((j == 0x7F).all()) for j in junk)
