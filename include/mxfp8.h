@@ -36,7 +36,7 @@
  *   - Workspace: the GEMM entry points may need device scratch -- split-K
  *     partial sums, and, for BF16 activations that go to a kernel reading E4M3
  *     (the tile kernels: more than 128 rows on large grids, more than 256 on
- *     small ones; the whole-K kernel: 17 to 64 rows, or fewer at K depths other
+ *     small ones; the whole-K kernel: 17 to 128 rows, or fewer at K depths other
  *     than 32 or 64 steps), the activations quantized to MXFP8 (the library
  *     quantizes BF16 input with mxfp8_quantize first).  The matching
  *     *_workspace_size(kind, shape) call gives the bytes (0 = none needed,
@@ -46,6 +46,10 @@
  *     Calls of any shape may therefore reuse one workspace one after another
  *     (same stream), but calls that run concurrently (other streams) must not
  *     share one.
+ *   - No entry point allocates, frees, synchronizes or records a memset: each
+ *     call is a fixed sequence of kernel launches on `stream`, so it can be
+ *     captured in a HIP graph.  A replay reuses the captured pointers, the
+ *     workspace included, which must stay allocated while the graph lives.
  *   - Non-finite inputs are outside the contract (codes then unspecified).
  *   - Results are deterministic: the same inputs give the same bytes, and BF16
  *     and pre-quantized activations give identical results (the split-K
