@@ -11,7 +11,9 @@ than the 256 MB Infinity Cache), so each step reads its weights cold, as the
 layers of a model do.
 
 Printed: one JSON line.  `value` is chain TFLOP/s at the configuration's token
-count; `ms_per_step` its time per call.  Besides the headline arm ("chain") it
+count; `ms_per_step` its time per call: the median of three timed rounds (after
+an untimed clock ramp), the arms interleaved within each round, with the spread
+of the rounds reported beside it.  Besides the headline arm ("chain") it
 reports the arm that hands the einsum BF16 x ("x_fused": the library quantizes it
 in the load path of the split-K decode kernel, otherwise into the workspace
 first) and the unfused arm ("unfused": BF16 z re-quantized by a separate
@@ -20,7 +22,10 @@ HIP events on the launch stream, the dominant kernel's roofline fraction, and th
 CPU oracle timed on this host's cores.  Per-kernel durations come from graphs of
 one kernel each, replayed back to back, so they compare with a profiler's kernel
 trace of the same command.  By default the line also carries the chain over 20
-token counts from 1 to 32768 ("sweep"), the standalone quantizer on the
+token counts from 1 to 32768 ("sweep": x drawn on the device, N(0, 1) with 0.1%
+of the entries x100 as in the decode / prefill / long configurations; each
+point the median of three rounds, and at 4096 and 32768 tokens also the
+per-kernel times and the roofline of the dominant kernel, "rooflines"), the standalone quantizer on the
 quantize-sweep rows ("quant_sweep") and the RMS-normalizing producer on the same
 rows ("producer_sweep"); --no-sweep --no-quant-sweep --no-producer-sweep leaves
 them out (profiling runs do, so that their kernel traces hold the configuration's
@@ -119,6 +124,29 @@ def cpu_baseline(cfg_name, inp, budget_s=12.0):
             "scalar_quantize": scalar_quantize_timing()}
 
 
+def cpu_long(block=1024):
+    """The oracle chain over all 32768 rows of the long configuration, in row blocks (the float64 x of every
+    row at once would take 8.6 GB), timed once; the input generation is outside the timed span."""
+    import synth_inputs as si
+    from oracle import chain_ref as cr
+
+    cfg = si.CHAIN_CONFIGS["long"]
+    inp = si.chain_inputs(cfg.shape, cfg.seed, cfg.outlier_rate)
+    t0 = time.perf_counter()
+    w = cr.quantize_weights(inp["wo_a"], inp["wo_b"])
+    t_w = time.perf_counter() - t0
+    x = inp["x"]
+    M = x.shape[0]
+    t0 = time.perf_counter()
+    for r0 in range(0, M, block):
+        cr.o_proj_chain(x[r0:r0 + block], *w)
+    el = time.perf_counter() - t0
+    flop = cfg.shape.flop
+    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": threads_used(), "kind": "oracle",
+            "sample": f"long: all {M} rows in blocks of {block}, timed once: {el:.1f} s "
+                      f"(+ {t_w:.1f} s to quantize the weights)", "seconds": el}
+
+
 def scalar_quantize_timing():
     """The oracle's scalar (pure-Python, exact-rational) quantizer, one thread, labelled "scalar": the tiny
     configuration's x and the quantize-sweep rows at M = 1 and 7 (larger M take minutes)."""
@@ -167,21 +195,71 @@ def time_arm_graphs(torch, graphs, stream, steps, warmup):
     return e0.elapsed_time(e1) / steps * 1e3
 
 
-def sweep(torch, L, Ms, dims, w, stream, args):
+def median_rounds(torch, graphs_by_arm, stream, reps, rounds=3, ramp_s=RAMP_S, calls_per_replay=1):
+    """µs per call of each arm: an untimed clock ramp (all arms replayed for ramp_s seconds), then `rounds`
+    rounds in which every arm's graph is replayed `reps` times and timed with HIP events on `stream`, the
+    arms interleaved within a round.  Returns {arm: {"us": median, "rounds": [...], "spread": max - min}}."""
+    t_ramp = time.perf_counter()
+    while time.perf_counter() - t_ramp < ramp_s:
+        with torch.cuda.stream(stream):
+            for g in graphs_by_arm.values():
+                g.replay()
+        torch.cuda.synchronize()
+    res = {a: [] for a in graphs_by_arm}
+    for _ in range(rounds):
+        for arm, g in graphs_by_arm.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            res[arm].append(e0.elapsed_time(e1) * 1e3 / (reps * calls_per_replay))
+    return {a: {"us": float(np.median(v)), "rounds": v, "spread": max(v) - min(v)} for a, v in res.items()}
+
+
+def roofline_block(kind, M, G, K, N, P, t_us, traffic=None):
+    """Roofline of one launch (the einsum or the GEMM) at M tokens from its average duration."""
+    flops = chain_flops(M, G, K, N, P)[kind]
+    nbytes = chain_bytes(M, G, K, N, P)[kind]
+    if flops / nbytes < FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        ach = nbytes / (t_us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": traffic, "kernel": KERNEL_NAMES[kind], "algorithmic_bytes_per_launch": nbytes,
+                "avg_launch_us": t_us}
+    ach = flops / (t_us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / FP8_PEAK_TFLOPS, "traffic": traffic, "kernel": KERNEL_NAMES[kind],
+            "algorithmic_flop_per_launch": flops, "avg_launch_us": t_us}
+
+
+def sweep_x(torch, M, G, K):
+    """BF16 [M, G*K] on the device: N(0, 1) with round(0.001 * numel) entries (positions drawn with
+    replacement) multiplied by 100 before the BF16 rounding, seeded per token count."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260100 + M)
+    x = torch.randn((M, G * K), generator=gen, device="cuda", dtype=torch.float32)
+    n_out = int(round(0.001 * x.numel()))
+    if n_out:
+        pos = torch.randint(0, x.numel(), (n_out,), generator=gen, device="cuda")
+        x.view(-1)[pos] *= 100.0
+    return x.to(torch.bfloat16)
+
+
+def sweep(torch, L, Ms, dims, w, stream, args, kernel_ms=(4096, 32768)):
     """µs/call of the chain, x_fused and unfused arms over token counts, weights rotated as in the headline
     run; `fusion_saving_us` = unfused - chain (what the MXFP8 epilogue saves against a separate requantize)."""
     G, K, N, P = dims
     out = []
-    gen = torch.Generator(device="cuda")
     for M in Ms:
-        gen.manual_seed(20260100 + M)
-        x = torch.randn((M, G * K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        x = sweep_x(torch, M, G, K)
         set_bytes = x.numel() * 2 + w["wa_q"].numel() + w["wb_q"].numel()
         R = int(min(8, max(1, -(-ROTATE_BYTES // set_bytes))))
         sets = [{"x": x if r == 0 else x.clone(),
                  "wa_q": w["wa_q"].clone(), "wa_sf": w["wa_sf"].clone(),
                  "wb_q": w["wb_q"].clone(), "wb_sf": w["wb_sf"].clone()} for r in range(R)]
-        res = {"M": M}
+        graphs = {}
         for arm in ("chain", "x_fused", "unfused"):
             # one graph with the chain once per rotating set, in a row (as consecutive layers)
             g = torch.cuda.CUDAGraph()
@@ -193,10 +271,15 @@ def sweep(torch, L, Ms, dims, w, stream, args):
                     for s in sets:
                         L.o_proj_chain(s["x"], s["wa_q"], s["wa_sf"], s["wb_q"], s["wb_sf"], mode=arm,
                                        stream=stream)
-            steps = max(5, min(args.steps, int(2e5 // max(1, M))))
-            reps = max(1, -(-steps // R))
-            res[f"{arm}_us"] = time_arm_graphs(torch, [g], stream, reps, max(1, reps // 4)) / R
-            del g
+            graphs[arm] = g
+        steps = max(6, min(args.steps, int(2e5 // max(1, M))))
+        reps = max(2, -(-steps // R))
+        timed = median_rounds(torch, graphs, stream, reps, ramp_s=0.1, calls_per_replay=R)
+        del graphs
+        res = {"M": M}
+        for arm in ("chain", "x_fused", "unfused"):
+            res[f"{arm}_us"] = timed[arm]["us"]
+            res[f"{arm}_spread_us"] = timed[arm]["spread"]
         flop = sum(chain_flops(M, G, K, N, P).values())
         nb = chain_bytes(M, G, K, N, P)
         us = res["chain_us"]
@@ -204,12 +287,58 @@ def sweep(torch, L, Ms, dims, w, stream, args):
         res["hbm_frac"] = sum(nb.values()) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
         res["mfma_frac"] = res["tflops"] / FP8_PEAK_TFLOPS
         res["fusion_saving_us"] = res["unfused_us"] - us
-        print(f"[bench] sweep M={M}: chain {us:.2f} us, x_fused {res['x_fused_us']:.2f} us, unfused "
-              f"{res['unfused_us']:.2f} us, {res['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        if M in kernel_ms:
+            res["kernels_avg_us"] = kernel_times(torch, L, sets, M, stream, args)
+            res["roofline"] = {k: roofline_block(k, M, G, K, N, P, res["kernels_avg_us"][KERNEL_NAMES[k]])
+                               for k in ("einsum", "gemm")}
+        print(f"[bench] sweep M={M}: chain {us:.2f} us (spread {res['chain_spread_us']:.2f}), x_fused "
+              f"{res['x_fused_us']:.2f} us, unfused {res['unfused_us']:.2f} us, {res['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
         out.append(res)
         del sets, x
         torch.cuda.empty_cache()
     return out
+
+
+def kernel_times(torch, L, sets, M, stream, args):
+    """Average µs per launch of each kernel of the chain at M tokens: one graph per kernel holding that launch
+    at least 16 times over the rotating sets, timed as the median of three rounds."""
+    G, N, K = sets[0]["wa_q"].shape
+    P = sets[0]["wb_q"].shape[0]
+    dev = sets[0]["x"].device
+    inter = {"x_q": torch.empty((M, G * K), dtype=torch.uint8, device=dev),
+             "x_sf": torch.empty((M, G * K // 128), dtype=torch.int32, device=dev),
+             "z_q": torch.empty((M, G * N), dtype=torch.uint8, device=dev),
+             "z_sf": torch.empty((M, G * N // 128), dtype=torch.int32, device=dev),
+             "out": torch.empty((M, P), dtype=torch.bfloat16, device=dev)}
+
+    def one(kind, s):
+        if kind == "quantize":
+            L.mxfp8_quantize(s["x"], q=inter["x_q"], sf=inter["x_sf"], stream=stream)
+        elif kind == "einsum":
+            L.grouped_fp8_einsum(inter["x_q"], inter["x_sf"], s["wa_q"], s["wa_sf"], out="mxfp8", z_q=inter["z_q"],
+                                 z_sf=inter["z_sf"], stream=stream)
+        else:
+            L.fp8_gemm_nt(inter["z_q"], inter["z_sf"], s["wb_q"], s["wb_sf"], d=inter["out"], stream=stream)
+
+    R = len(sets)
+    reps = max(1, -(-16 // R))
+    graphs = {}
+    for kind in ("quantize", "einsum", "gemm"):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for s in sets:
+                one(kind, s)
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(reps):
+                    for s in sets:
+                        one(kind, s)
+        torch.cuda.synchronize()
+        graphs[kind] = g
+    n = max(2, min(args.steps, 200) // (reps * R))
+    timed = median_rounds(torch, graphs, stream, n, ramp_s=0.1, calls_per_replay=reps * R)
+    return {KERNEL_NAMES[k]: v["us"] for k, v in timed.items()}
 
 
 def quant_sweep(torch, L, si, stream, args):
@@ -321,6 +450,9 @@ def main():
     ap.add_argument("--producer-sweep", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the RMS-normalizing MXFP8 producer on the quantize-sweep rows (M x 7168), "
                          "next to the standalone quantizer it replaces")
+    ap.add_argument("--cpu-long", action="store_true",
+                    help="also time the oracle chain once on all 32768 rows of the long configuration, in blocks "
+                         "of 1024 rows (several minutes of CPU work; off by default)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -414,72 +546,34 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def time_graphs(g, steps, warmup):
-        """µs per chain call: replays of the R-chain graph covering at least `steps` calls."""
-        n_rep, n_warm = max(1, -(-steps // R)), max(1, -(-warmup // R))
-        with torch.cuda.stream(stream):
+    # The arms, each one graph of R chains, timed as the median of three rounds after a clock ramp (after the
+    # idle host-side set-up the device's clocks take milliseconds of load to ramp up: the first arm timed
+    # after a short warm-up read 10-15% slow), the arms interleaved within each round.
+    arms = [a for a in args.arms.split(",") if a]
+    graphs = {arm: capture(arm) for arm in arms}
+    n_warm = max(1, -(-args.warmup // R))
+    with torch.cuda.stream(stream):
+        for g in graphs.values():
             for _ in range(n_warm):
                 g.replay()
-        torch.cuda.synchronize()
-        # After the idle host-side set-up the device's clocks take milliseconds of load to ramp
-        # up: the first arm timed after a short warm-up read 10-15% slow.  Keep replaying,
-        # untimed, until RAMP_S seconds of load have passed.
-        t_ramp = time.perf_counter()
-        while time.perf_counter() - t_ramp < RAMP_S:
-            with torch.cuda.stream(stream):
-                for _ in range(4):
-                    g.replay()
-            torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(n_rep):
-                g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / (n_rep * R), wall / (n_rep * R) * 1e3
-
-    arms = [a for a in args.arms.split(",") if a]
+    torch.cuda.synchronize()
+    timed = median_rounds(torch, graphs, stream, max(1, -(-args.steps // R)), calls_per_replay=R)
+    del graphs
     results = {}
     for arm in arms:
-        g = capture(arm)
-        ms_ev, ms_wall = time_graphs(g, args.steps, args.warmup)
-        results[arm] = {"us_per_call": ms_ev * 1e3, "wall_us_per_call": ms_wall * 1e3}
-        print(f"[bench] arm {arm}: {ms_ev * 1e3:.2f} us/call (graph replay)", file=sys.stderr, flush=True)
-        del g
+        results[arm] = {"us_per_call": timed[arm]["us"], "rounds_us": timed[arm]["rounds"],
+                        "spread_us": timed[arm]["spread"]}
+        print(f"[bench] arm {arm}: {timed[arm]['us']:.2f} us/call (graph replay, median of "
+              f"{len(timed[arm]['rounds'])} rounds, spread {timed[arm]['spread']:.2f})", file=sys.stderr,
+              flush=True)
 
     # Per-kernel durations: each launch of the headline chain captured alone in one
     # graph, at least 16 times in a row over the rotating sets (inputs stay cold), and
     # the graph replayed and timed with HIP events on the launch stream -- the kernel's
     # own duration plus the small gap between graph nodes, comparable with a
     # profiler's kernel trace (one launch per graph would time the host's submission).
-    def launch_one(kind, s):
-        if kind == "quantize":
-            L.mxfp8_quantize(s["x"], q=s["x_q"], sf=s["x_sf"], stream=stream)
-        elif kind == "einsum":
-            L.grouped_fp8_einsum(s["x_q"], s["x_sf"], s["wa_q"], s["wa_sf"], out="mxfp8", z_q=s["z_q"],
-                                 z_sf=s["z_sf"], stream=stream)
-        else:
-            L.fp8_gemm_nt(s["z_q"], s["z_sf"], s["wb_q"], s["wb_sf"], d=s["out"], stream=stream)
-
-    t_k = {}
-    reps = max(1, -(-16 // R))                     # at least 16 launches per graph
-    for kind in ("quantize", "einsum", "gemm"):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for s in sets:
-                launch_one(kind, s)
-            stream.synchronize()
-            with torch.cuda.graph(g, stream=stream):
-                for _ in range(reps):
-                    for s in sets:
-                        launch_one(kind, s)
-        torch.cuda.synchronize()
-        t_k[kind] = time_arm_graphs(torch, [g], stream, max(1, args.steps // (reps * R)) + 1,
-                                    max(1, args.warmup // (reps * R))) / (reps * R)
-        del g
+    t_k = {k: v for k, v in zip(("quantize", "einsum", "gemm"),
+                                kernel_times(torch, L, sets, M, stream, args).values())}
 
     flops = chain_flops(M, G, K, N, P)
     nbytes = chain_bytes(M, G, K, N, P)
@@ -489,9 +583,6 @@ def main():
     value = total_flop / (us * 1e-6) / 1e12
 
     dom = max(("einsum", "gemm"), key=lambda k: t_k[k])
-    t_dom = t_k[dom]
-    hbm_bound = (flops[dom] / nbytes[dom]) < (FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3)
-    kern_name = KERNEL_NAMES[dom]
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
     if os.path.exists(tpath):
@@ -499,16 +590,7 @@ def main():
             tr = json.load(f)
         if tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = tr.get(dom, {}).get("hbm_bytes_per_launch")
-    if hbm_bound:
-        ach = nbytes[dom] / (t_dom * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                "traffic": traffic, "kernel": kern_name, "algorithmic_bytes_per_launch": nbytes[dom],
-                "avg_launch_us": t_dom}
-    else:
-        ach = flops[dom] / (t_dom * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / FP8_PEAK_TFLOPS, "traffic": traffic, "kernel": kern_name,
-                "algorithmic_flop_per_launch": flops[dom], "avg_launch_us": t_dom}
+    roof = roofline_block(dom, M, G, K, N, P, t_k[dom], traffic)
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -521,6 +603,7 @@ def main():
                    "weights": "MXFP8 of BF16 N(0,0.02)", "rotating_sets": R, "timing": "HIP graph replay"},
         "us_per_call": us,
         "arms_us_per_call": {a: r["us_per_call"] for a, r in results.items()},
+        "arms_rounds_us": {a: r["rounds_us"] for a, r in results.items()},
         "fusion_saving_us": (results["unfused"]["us_per_call"] - us) if "unfused" in results else None,
         "kernels_avg_us": {KERNEL_NAMES[k]: v for k, v in t_k.items()},
         "hbm_roofline_frac_chain": sum(nbytes.values()) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -531,6 +614,12 @@ def main():
     if args.sweep:
         line["sweep"] = sweep(torch, L, [int(v) for v in args.sweep.split(",") if v], (G, K, N, P),
                               sets[0], stream, args)
+        # the dominant kernel's roofline at the prefill (4096) and long (32768) token counts as well
+        line["rooflines"] = {"decode": roof}
+        for pt in line["sweep"]:
+            if "roofline" in pt:
+                name = {4096: "prefill", 32768: "long"}.get(pt["M"], f"M={pt['M']}")
+                line["rooflines"][name] = max(pt["roofline"].values(), key=lambda r: r["avg_launch_us"])
     if args.quant_sweep:
         line["quant_sweep"] = quant_sweep(torch, L, si, stream, args)
     if args.producer_sweep:
@@ -538,6 +627,9 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.config, inp)
+    if args.cpu_long:
+        print("[bench] timing the CPU oracle on every row of the long configuration", file=sys.stderr, flush=True)
+        line["cpu_long"] = cpu_long()
     print(json.dumps(line), flush=True)
 
 

@@ -51,6 +51,9 @@
  *     captured in a HIP graph.  A replay reuses the captured pointers, the
  *     workspace included, which must stay allocated while the graph lives.
  *   - Non-finite inputs are outside the contract (codes then unspecified).
+ *   - The library keeps no mutable global state: every call's behaviour is a
+ *     function of its arguments (the only cache is the per-device result of
+ *     the architecture check), so calls from several threads are safe.
  *   - Results are deterministic: the same inputs give the same bytes, and BF16
  *     and pre-quantized activations give identical results (the split-K
  *     streaming kernel quantizes BF16 in its load path with the quantizer's
@@ -95,24 +98,6 @@ int mxfp8_version(void);
 
 /* MXFP8_OK when the current HIP device is a gfx950, else MXFP8_ERR_DEVICE. */
 int mxfp8_device_check(void);
-
-/*
- * mxfp8_set_splitk_mode -- how the few-token (decode) GEMM kernels combine the
- * fp32 partial tiles of a K range split across workgroups.  Diagnostic control:
- * every mode gives the same bits, only the time differs.
- *
- *   0  (default) through the L2 cache of one XCD: the splits of a tile are
- *      consecutive workgroups, which round-robin dispatch places on one XCD.
- *      The arrival counter records each split's XCD; if any split ran on another
- *      XCD, the last split to arrive computes the other splits again itself.
- *   1  through memory (write-through stores, read back past the caches).
- *   2  as 0, but the last split always recomputes the others (exercises the
- *      fallback of mode 0).
- *
- * Applies to launches made after the call, process-wide.  Returns MXFP8_OK, or
- * MXFP8_ERR_UNSUPPORTED for another value (the mode is then unchanged).
- */
-int mxfp8_set_splitk_mode(int mode);
 
 /*
  * mxfp8_quantize -- dynamic MXFP8 quantization of BF16 rows

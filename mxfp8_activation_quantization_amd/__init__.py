@@ -16,7 +16,7 @@ from .binding import (  # noqa: F401
     MXFP8ArgumentError,
     MXFP8Error,
     device_check,
-    set_splitk_mode,
+    release_retained_workspaces,
     fp8_gemm_nt,
     grouped_fp8_einsum,
     lib,

@@ -39,7 +39,6 @@ SIGNATURES = {
     "mxfp8_status_string": (ctypes.c_char_p, [c_int]),
     "mxfp8_version": (c_int, []),
     "mxfp8_device_check": (c_int, []),
-    "mxfp8_set_splitk_mode": (c_int, [c_int]),
     "mxfp8_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "mxfp8_rmsnorm_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, c_vp, c_i64, c_vp, c_i64,
                                        c_vp, c_i64, c_vp]),
@@ -49,6 +48,11 @@ SIGNATURES = {
     "fp8_gemm_nt": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64,
                             c_vp, c_i64, c_vp]),
     "fp8_gemm_nt_workspace_size": (c_i64, [c_int, c_i64, c_i64, c_i64]),
+    # include/mxfp8_testing.h: the same calls with the split-K combine chosen per call
+    "mxfp8_testing_grouped_fp8_einsum": (c_int, [c_int, c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                                 c_vp, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "mxfp8_testing_fp8_gemm_nt": (c_int, [c_int, c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                          c_vp, c_i64, c_vp, c_i64, c_vp]),
 }
 
 
@@ -108,12 +112,23 @@ def _rows(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise ValueError(f"{name}: expected a device tensor")
 
 
-# Split-K scratch: one zero-filled buffer per (device, stream), grown on demand.  The
-# kernels leave its counters at zero, so a buffer is reusable by later calls on
-# the same stream (stream order serializes them).  An outgrown buffer is kept, not
-# freed: a graph captured earlier holds its device address and replays into it.
+# Scratch of the GEMM calls (split-K counters and partials, staged activations): one
+# zero-filled buffer per (device, stream), grown on demand.  The kernels leave its
+# counters at zero, so a buffer is reusable by later calls on the same stream (stream
+# order serializes them).  A buffer handed out while its stream was being captured
+# into a graph is marked: the graph replays into its address, so when the stream's
+# workspace later grows, a marked buffer is kept (in _retained) and an unmarked one is
+# released.  A workspace cannot be created or grown during capture (the zero fill would
+# only be recorded, leaving the counters undefined until the first replay): warm the
+# capture stream with one eager call of the largest shape first, or pass `workspace=`.
 _workspaces: dict = {}
-_outgrown: list = []
+_captured: set = set()          # keys of _workspaces whose current buffer a graph holds
+_retained: list = []            # outgrown buffers that a captured graph may still use
+
+
+def _stream_obj(stream_ptr: int):
+    cur = torch.cuda.current_stream()
+    return cur if cur.cuda_stream == stream_ptr else torch.cuda.ExternalStream(stream_ptr)
 
 
 def workspace_for(nbytes: int, device: torch.device, stream_ptr: int) -> torch.Tensor | None:
@@ -121,12 +136,33 @@ def workspace_for(nbytes: int, device: torch.device, stream_ptr: int) -> torch.T
         return None
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_ptr)
     ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        if ws is not None:
-            _outgrown.append(ws)
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+    st = _stream_obj(stream_ptr)
+    with torch.cuda.stream(st):
+        capturing = torch.cuda.is_current_stream_capturing()
+        if ws is None or ws.numel() < nbytes:
+            if capturing:
+                raise RuntimeError(
+                    f"the GEMM needs a {nbytes}-byte workspace on a stream that is being captured, and none of "
+                    "that size exists yet; make one eager call of the largest shape on this stream before "
+                    "capturing, or pass workspace=")
+            if ws is not None and key in _captured:
+                _retained.append(ws)
+            _captured.discard(key)
+            # allocated and zero-filled on the stream its kernels run on: the fill is stream-ordered before
+            # them, and the caching allocator reuses a released buffer only in that stream's order
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
+    if capturing:
+        _captured.add(key)
     return ws
+
+
+def release_retained_workspaces() -> int:
+    """Drops the outgrown workspaces kept for captured graphs; call once those graphs are destroyed.
+    Returns how many buffers were released."""
+    n = len(_retained)
+    _retained.clear()
+    return n
 
 
 def _ws_args(need: int, device, stream_ptr: int, workspace: torch.Tensor | None):
@@ -140,12 +176,9 @@ def device_check() -> None:
     _check(_lib.mxfp8_device_check(), "mxfp8_device_check")
 
 
+# How the decode kernels combine split-K partials; every mode gives the same bits.  Anything but
+# "local" goes through the test-only entry points of include/mxfp8_testing.h.
 SPLITK_MODES = {"local": 0, "through": 1, "recompute": 2}
-
-
-def set_splitk_mode(mode: str) -> None:
-    """How the decode kernels combine split-K partials ("local", "through", "recompute"); same bits."""
-    _check(_lib.mxfp8_set_splitk_mode(SPLITK_MODES[mode]), "mxfp8_set_splitk_mode")
 
 
 # ----------------------------------------------------------------------------- quantize
@@ -221,12 +254,14 @@ def _act_args(x: torch.Tensor, x_sf: torch.Tensor | None):
 
 def grouped_fp8_einsum(x: torch.Tensor, x_sf: torch.Tensor | None, w: torch.Tensor, w_sf: torch.Tensor, *,
                        out: str = "mxfp8", z_q: torch.Tensor | None = None, z_sf: torch.Tensor | None = None,
-                       z_bf16: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+                       z_bf16: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+                       splitk_combine: str = "local"):
     """wo_a: z[m, g*N+n] = sum_k x[m, g*K+k] w[g, n, k].
 
     x: BF16 [M, G*K] (quantized in the kernel) or E4M3 uint8 [M, G*K] with x_sf int32 [M, G*K/128].
     w: uint8 [G, N, K], w_sf: int32 [G, N, K/128].
     out: "mxfp8" -> (z_q, z_sf); "bf16" -> z_bf16; "both" -> (z_q, z_sf, z_bf16).
+    splitk_combine: "local" (the product path), or "through" / "recompute" (test-only entry point).
     """
     if w.dim() != 3 or w.dtype != torch.uint8 or w_sf.dtype != torch.int32:
         raise ValueError("w must be uint8 [G, N, K] and w_sf int32 [G, N, K/128]")
@@ -257,11 +292,15 @@ def grouped_fp8_einsum(x: torch.Tensor, x_sf: torch.Tensor | None, w: torch.Tens
         z_bf16 = None
     sp = _stream(stream)
     wsp, wsn = _ws_args(_lib.grouped_fp8_einsum_workspace_size(kind, M, G, K, N), dev, sp, workspace)
-    _check(_lib.grouped_fp8_einsum(kind, xp, ldx, xsfp, ldxsf, M, G, K, N, _ptr(w), _ptr(w_sf),
-                                   _ptr(z_q), z_q.stride(0) if z_q is not None else 0,
-                                   _ptr(z_sf), z_sf.stride(0) if z_sf is not None else 0,
-                                   _ptr(z_bf16), z_bf16.stride(0) if z_bf16 is not None else 0,
-                                   wsp, wsn, sp), "grouped_fp8_einsum")
+    args = (kind, xp, ldx, xsfp, ldxsf, M, G, K, N, _ptr(w), _ptr(w_sf),
+            _ptr(z_q), z_q.stride(0) if z_q is not None else 0,
+            _ptr(z_sf), z_sf.stride(0) if z_sf is not None else 0,
+            _ptr(z_bf16), z_bf16.stride(0) if z_bf16 is not None else 0, wsp, wsn, sp)
+    if splitk_combine == "local":
+        _check(_lib.grouped_fp8_einsum(*args), "grouped_fp8_einsum")
+    else:
+        _check(_lib.mxfp8_testing_grouped_fp8_einsum(SPLITK_MODES[splitk_combine], *args),
+               "mxfp8_testing_grouped_fp8_einsum")
     if out == "mxfp8":
         return z_q, z_sf
     if out == "bf16":
@@ -272,8 +311,10 @@ def grouped_fp8_einsum(x: torch.Tensor, x_sf: torch.Tensor | None, w: torch.Tens
 # ----------------------------------------------------------------------------- gemm
 
 def fp8_gemm_nt(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_sf: torch.Tensor,
-                d: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """wo_b: d[m, n] = bf16(sum_k a[m, k] b[n, k]); a BF16 or E4M3 (+ a_sf), b uint8 [N, K] + b_sf int32 [N, K/128]."""
+                d: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+                splitk_combine: str = "local") -> torch.Tensor:
+    """wo_b: d[m, n] = bf16(sum_k a[m, k] b[n, k]); a BF16 or E4M3 (+ a_sf), b uint8 [N, K] + b_sf int32 [N, K/128].
+    splitk_combine as in grouped_fp8_einsum."""
     if b.dim() != 2 or b.dtype != torch.uint8 or b_sf.dtype != torch.int32:
         raise ValueError("b must be uint8 [N, K] and b_sf int32 [N, K/128]")
     if not (b.is_contiguous() and b_sf.is_contiguous()):
@@ -286,8 +327,11 @@ def fp8_gemm_nt(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_s
     _rows(d, torch.bfloat16, "d")
     sp = _stream(stream)
     wsp, wsn = _ws_args(_lib.fp8_gemm_nt_workspace_size(kind, M, N, K), a.device, sp, workspace)
-    _check(_lib.fp8_gemm_nt(kind, ap, lda, asfp, ldasf, M, N, K, _ptr(b), _ptr(b_sf), _ptr(d), d.stride(0),
-                            wsp, wsn, sp), "fp8_gemm_nt")
+    args = (kind, ap, lda, asfp, ldasf, M, N, K, _ptr(b), _ptr(b_sf), _ptr(d), d.stride(0), wsp, wsn, sp)
+    if splitk_combine == "local":
+        _check(_lib.fp8_gemm_nt(*args), "fp8_gemm_nt")
+    else:
+        _check(_lib.mxfp8_testing_fp8_gemm_nt(SPLITK_MODES[splitk_combine], *args), "mxfp8_testing_fp8_gemm_nt")
     return d
 
 

@@ -3,7 +3,7 @@
 // Every argument is checked on the host before the first HIP call, so argument
 // errors are reported the same way on a machine without a GPU.  The library
 // allocates nothing, never synchronizes, and keeps no state besides a per-device
-// cache of the architecture check and the split-K combine mode.
+// cache of the architecture check.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -36,7 +36,6 @@ bool overlaps(const Range& a, const Range& b) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 std::atomic<int> g_arch_cache[256];  // 0 = unknown, 1 = gfx950, 2 = other
-std::atomic<int> g_splitk_mode{mx::SPLITK_LOCAL};   // see mxfp8_set_splitk_mode
 
 int device_check() {
   int dev = -1;
@@ -138,12 +137,6 @@ MX_API int mxfp8_version(void) { return 100; }
 
 MX_API int mxfp8_device_check(void) { return device_check(); }
 
-MX_API int mxfp8_set_splitk_mode(int mode) {
-  if (mode < mx::SPLITK_LOCAL || mode > mx::SPLITK_RECOMPUTE) return MXFP8_ERR_UNSUPPORTED;
-  g_splitk_mode.store(mode, std::memory_order_relaxed);
-  return MXFP8_OK;
-}
-
 MX_API int mxfp8_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, void* q, int64_t ld_q,
                           int32_t* sf, int64_t ld_sf, void* stream) {
   if (M < 0 || K <= 0 || K % 128) return MXFP8_ERR_SHAPE;
@@ -189,10 +182,13 @@ MX_API int mxfp8_rmsnorm_quantize(const void* x, int64_t M, int64_t K, int64_t l
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
-MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf,
-                              int64_t M, int64_t G, int64_t K, int64_t N, const void* w, const int32_t* w_sf,
-                              void* z_q, int64_t ld_z, int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb,
-                              void* workspace, int64_t workspace_bytes, void* stream) {
+namespace {
+
+int einsum_impl(int splitk_mode, int x_kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf,
+                int64_t M, int64_t G, int64_t K, int64_t N, const void* w, const int32_t* w_sf, void* z_q,
+                int64_t ld_z, int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb, void* workspace,
+                int64_t workspace_bytes, void* stream) {
+  if (splitk_mode < mx::SPLITK_LOCAL || splitk_mode > mx::SPLITK_RECOMPUTE) return MXFP8_ERR_UNSUPPORTED;
   if (M < 0 || G < 1 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
   if (G > 65535 || K > kMaxDepth || M > INT32_MAX || G * N > INT32_MAX) return MXFP8_ERR_SHAPE;
   const int64_t cols_in = G * K, cols_out = G * N;
@@ -223,7 +219,7 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
   if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2]))
     return MXFP8_ERR_ALIAS;
   mx::GemmArgs p{};
-  p.splitk_mode = g_splitk_mode.load(std::memory_order_relaxed);
+  p.splitk_mode = splitk_mode;
   Range rw;
   const mx::GemmPlan plan = mx::plan_gemm(M, G, N, K, x_kind == MXFP8_ACT_BF16);
   if (int s = bind_workspace(plan, workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
@@ -244,9 +240,14 @@ MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
-MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf, int64_t M,
-                       int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
-                       void* workspace, int64_t workspace_bytes, void* stream) {
+}  // namespace
+
+namespace mx {
+
+int gemm_entry(int splitk_mode, int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf,
+               int64_t M, int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
+               void* workspace, int64_t workspace_bytes, void* stream) {
+  if (splitk_mode < mx::SPLITK_LOCAL || splitk_mode > mx::SPLITK_RECOMPUTE) return MXFP8_ERR_UNSUPPORTED;
   if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
   if (K > kMaxDepth || M > INT32_MAX || N > INT32_MAX) return MXFP8_ERR_SHAPE;
   if (int s = check_act(a_kind, a, ld_a, a_sf, ld_asf, M, K); s != MXFP8_OK) return s;
@@ -263,7 +264,7 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
   for (const Range& in : ins)
     if (overlaps(out, in)) return MXFP8_ERR_ALIAS;
   mx::GemmArgs p{};
-  p.splitk_mode = g_splitk_mode.load(std::memory_order_relaxed);
+  p.splitk_mode = splitk_mode;
   Range rw;
   const mx::GemmPlan plan = mx::plan_gemm(M, 1, N, K, a_kind == MXFP8_ACT_BF16);
   if (int s = bind_workspace(plan, workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
@@ -278,6 +279,41 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
   p.zb = static_cast<uint16_t*>(d); p.ld_zb = ld_d;
   const hipError_t e = launch(p, plan, 1, a_kind == MXFP8_ACT_BF16, 1, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
+}  // namespace mx
+
+MX_API int grouped_fp8_einsum(int x_kind, const void* x, int64_t ld_x, const int32_t* x_sf, int64_t ld_xsf,
+                              int64_t M, int64_t G, int64_t K, int64_t N, const void* w, const int32_t* w_sf,
+                              void* z_q, int64_t ld_z, int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  return einsum_impl(mx::SPLITK_LOCAL, x_kind, x, ld_x, x_sf, ld_xsf, M, G, K, N, w, w_sf, z_q, ld_z, z_sf, ld_zsf,
+                     z_bf16, ld_zb, workspace, workspace_bytes, stream);
+}
+
+MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf, int64_t M,
+                       int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  return mx::gemm_entry(mx::SPLITK_LOCAL, a_kind, a, ld_a, a_sf, ld_asf, M, N, K, b, b_sf, d, ld_d, workspace,
+                        workspace_bytes, stream);
+}
+
+// Test-only forms (include/mxfp8_testing.h): the same calls with the split-K combine chosen per call.
+MX_API int mxfp8_testing_grouped_fp8_einsum(int splitk_combine, int x_kind, const void* x, int64_t ld_x,
+                                            const int32_t* x_sf, int64_t ld_xsf, int64_t M, int64_t G, int64_t K,
+                                            int64_t N, const void* w, const int32_t* w_sf, void* z_q, int64_t ld_z,
+                                            int32_t* z_sf, int64_t ld_zsf, void* z_bf16, int64_t ld_zb,
+                                            void* workspace, int64_t workspace_bytes, void* stream) {
+  return einsum_impl(splitk_combine, x_kind, x, ld_x, x_sf, ld_xsf, M, G, K, N, w, w_sf, z_q, ld_z, z_sf, ld_zsf,
+                     z_bf16, ld_zb, workspace, workspace_bytes, stream);
+}
+
+MX_API int mxfp8_testing_fp8_gemm_nt(int splitk_combine, int a_kind, const void* a, int64_t ld_a,
+                                     const int32_t* a_sf, int64_t ld_asf, int64_t M, int64_t N, int64_t K,
+                                     const void* b, const int32_t* b_sf, void* d, int64_t ld_d, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+  return mx::gemm_entry(splitk_combine, a_kind, a, ld_a, a_sf, ld_asf, M, N, K, b, b_sf, d, ld_d, workspace,
+                        workspace_bytes, stream);
 }
 
 MX_API int64_t grouped_fp8_einsum_workspace_size(int x_kind, int64_t M, int64_t G, int64_t K, int64_t N) {

@@ -13,7 +13,8 @@ import pytest
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-HEADER = os.path.join(os.path.dirname(HERE), "include", "mxfp8.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 mx = pytest.importorskip("mxfp8_activation_quantization_amd",
                          reason="libmxfp8.so is not built (run the build first)")
@@ -23,10 +24,13 @@ LIB = B.lib()
 HAVE_GPU = torch.cuda.is_available()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_chain_entry_points():
@@ -37,9 +41,20 @@ def test_header_declares_the_chain_entry_points():
 
 
 def test_library_exports_every_declared_symbol():
+    assert len(HEADERS) >= 2
     for n in declared_functions():
         assert hasattr(LIB, n), n
         assert n in B.SIGNATURES, n
+
+
+def test_product_header_has_no_global_state_setter():
+    """The product ABI keeps no mutable global state: the split-K combine is a per-call argument of the
+    test-only entry points (include/mxfp8_testing.h), not a process-wide switch."""
+    product = declared_functions([os.path.join(INCLUDE, "mxfp8.h")])
+    assert not any("set_" in n for n in product)
+    assert not hasattr(LIB, "mxfp8_set_splitk_mode")
+    testing = declared_functions([os.path.join(INCLUDE, "mxfp8_testing.h")])
+    assert testing == ["mxfp8_testing_fp8_gemm_nt", "mxfp8_testing_grouped_fp8_einsum"]
 
 
 def test_status_strings():
@@ -236,11 +251,25 @@ def test_workspace_errors():
     assert gemm(K=512, ws=None, ws_bytes=0) != B.MXFP8_ERR_WORKSPACE      # one K slice: none needed
 
 
-def test_splitk_mode_control():
-    assert LIB.mxfp8_set_splitk_mode(3) == B.MXFP8_ERR_UNSUPPORTED
-    assert LIB.mxfp8_set_splitk_mode(-1) == B.MXFP8_ERR_UNSUPPORTED
-    for m in (1, 2, 0):
-        assert LIB.mxfp8_set_splitk_mode(m) == B.MXFP8_OK
+def test_splitk_combine_argument_of_the_testing_entry_points():
+    """Modes 0-2 pass validation (and then need the device); anything else is rejected before any HIP call."""
+    def t_gemm(mode, **kw):
+        return LIB.mxfp8_testing_fp8_gemm_nt(mode, B.MXFP8_ACT_MXFP8, X, 4096, SF, 32, 4, 256, 4096, W, WSF, D, 256,
+                                             WS, 1 << 30, None)
+
+    def t_einsum(mode):
+        return LIB.mxfp8_testing_grouped_fp8_einsum(mode, B.MXFP8_ACT_MXFP8, X, 512, SF, 4, 4, 2, 256, 128, W, WSF,
+                                                    Z, 256, ZSF, 2, None, 0, WS, 1 << 30, None)
+
+    for f in (t_gemm, t_einsum):
+        assert f(3) == B.MXFP8_ERR_UNSUPPORTED
+        assert f(-1) == B.MXFP8_ERR_UNSUPPORTED
+        if not HAVE_GPU:
+            for m in (0, 1, 2):
+                assert f(m) == B.MXFP8_ERR_DEVICE
+    # an argument error is reported as such whatever the mode
+    assert LIB.mxfp8_testing_fp8_gemm_nt(1, B.MXFP8_ACT_MXFP8, X, 4096, SF, 32, 4, 100, 4096, W, WSF, D, 256,
+                                         WS, 1 << 30, None) == B.MXFP8_ERR_SHAPE
 
 
 def test_binding_raises_value_error_on_argument_status():

@@ -15,12 +15,12 @@ The shapes are the DeepSeek-V4.1-Flash TP1 o_proj of vLLM PR #60118
     maximum within one BF16 step of a power-of-two threshold;
   * the wo_b GEMM fed the oracle's own z: BF16 output within 2e-2 of each row's
     RMS (max |err| / RMS);
-  * the whole chain: |out - out64| <= 2e-2 * RMS(row) plus the propagation
-    through |wo_b| of the z deviations the z bar admits.  gfx950's FP8 MFMA
-    aligns the products of one dot product to the largest with about twelve
-    fractional bits, so a few BF16 z values land one rounding step away from
-    the float64 value and flip a code by one ulp; each such flip moves the
-    output by |dz| * |wo_b|, which this bound charges exactly.
+  * the whole chain: max |out - out64| / RMS(row) <= 2e-2 on every row checked
+    (the bar as stated, no allowance).  The propagation through |wo_b| of the z
+    code flips that the z bar admits is printed beside it as a diagnostic:
+    gfx950's FP8 MFMA aligns the products of one dot product to the largest
+    with about twelve fractional bits, so a few BF16 z values land one rounding
+    step away from the float64 value and flip a code by one ulp.
 """
 import numpy as np
 import pytest
@@ -311,17 +311,14 @@ def test_split_k_combine_modes_give_identical_bits(lib, kind, M, G, N, K):
     assert need > 0                                                       # the shape is split along K
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     outs = {}
-    try:
-        for mode in ("local", "through", "recompute", "local"):
-            lib.set_splitk_mode(mode)
-            if kind == "gemm":
-                outs[mode] = to_np(lib.fp8_gemm_nt(a_t, asf_t, w_t, wsf_t, workspace=ws))
-            else:
-                outs[mode] = to_np(lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="bf16", workspace=ws))
-            torch.cuda.synchronize()
-            assert int(ws[:4096].view(torch.int32).abs().sum()) == 0, mode
-    finally:
-        lib.set_splitk_mode("local")
+    for mode in ("local", "through", "recompute", "local"):
+        if kind == "gemm":
+            outs[mode] = to_np(lib.fp8_gemm_nt(a_t, asf_t, w_t, wsf_t, workspace=ws, splitk_combine=mode))
+        else:
+            outs[mode] = to_np(lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="bf16", workspace=ws,
+                                                      splitk_combine=mode))
+        torch.cuda.synchronize()
+        assert int(ws[:4096].view(torch.int32).abs().sum()) == 0, mode
     assert np.array_equal(outs["through"], outs["local"])
     assert np.array_equal(outs["recompute"], outs["local"])
     if kind == "gemm":
@@ -349,24 +346,22 @@ def _modes_bitexact(lib, kind, M, G, N, K, seed, modes=("local", "through", "rec
         ref = mx.bf16_round(cr.grouped_einsum(aq, asf, wq.reshape(G, N, K), wsf.reshape(G, N, K // 128), G, K, N))
         oq, osf = mx.quantize(ref)
         w_t, wsf_t = u8_to_dev(wq.reshape(G, N, K)), i32_to_dev(wsf.reshape(G, N, K // 128))
-    try:
-        for mode in modes:
-            lib.set_splitk_mode(mode)
-            if kind == "gemm":
-                d = lib.fp8_gemm_nt(a_t, asf_t, w_t, wsf_t, workspace=ws)
-                assert np.array_equal(to_np(d), ref), mode
-            else:
-                z_q, z_sf, z_b = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="both", workspace=ws)
-                assert np.array_equal(to_np(z_b), ref), mode
-                assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf), mode
-                z_q2, z_sf2 = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="mxfp8", workspace=ws)
-                assert torch.equal(z_q2, z_q) and torch.equal(z_sf2, z_sf), mode
-                z_b2 = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="bf16", workspace=ws)
-                assert torch.equal(z_b2, z_b), mode
-            torch.cuda.synchronize()
-            assert int(ws[:65536].view(torch.int32).abs().sum()) == 0, mode
-    finally:
-        lib.set_splitk_mode("local")
+    for mode in modes:
+        if kind == "gemm":
+            d = lib.fp8_gemm_nt(a_t, asf_t, w_t, wsf_t, workspace=ws, splitk_combine=mode)
+            assert np.array_equal(to_np(d), ref), mode
+        else:
+            z_q, z_sf, z_b = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="both", workspace=ws,
+                                                    splitk_combine=mode)
+            assert np.array_equal(to_np(z_b), ref), mode
+            assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf), mode
+            z_q2, z_sf2 = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="mxfp8", workspace=ws,
+                                                 splitk_combine=mode)
+            assert torch.equal(z_q2, z_q) and torch.equal(z_sf2, z_sf), mode
+            z_b2 = lib.grouped_fp8_einsum(a_t, asf_t, w_t, wsf_t, out="bf16", workspace=ws, splitk_combine=mode)
+            assert torch.equal(z_b2, z_b), mode
+        torch.cuda.synchronize()
+        assert int(ws[:65536].view(torch.int32).abs().sum()) == 0, mode
 
 
 @pytest.mark.parametrize("M", [1, 20, 33, 64])
@@ -542,19 +537,20 @@ def test_whole_k_bf16_activations_equal_prequantized(lib, kind, M, G, N, K):
     assert torch.equal(zq, a[0]) and torch.equal(zsf, a[1])
 
 
-def check_out_against_oracle(c, out, z_q, z_sf, ref):
-    """Chain output within 2e-2 * row RMS plus the propagated z deviations admitted by the z bar."""
+def check_out_against_oracle(c, out, z_q, z_sf, ref, label=""):
+    """Chain output: max |out - out64| / RMS(row) <= 2e-2 on every row.  The statistics (max, p99.9, rows over
+    the bar) and, as a diagnostic only, how far the z code flips propagate through |wo_b| are printed first."""
     o = mx.bf16_decode(to_np(out))
     rms = np.sqrt(np.mean(ref.out64 ** 2, axis=1, keepdims=True))
+    err = np.abs(o - ref.out64)
+    rel = np.max(err / np.maximum(rms, 1e-30), axis=1)
     dz = np.abs(mx.dequantize(to_np(z_q), to_np(z_sf)) - mx.dequantize(ref.z_q, ref.z_sf))
     wb = np.abs(mx.dequantize(c.o_w[2], c.o_w[3]))
     prop = dz @ wb.T
-    err = np.abs(o - ref.out64)
-    rel = np.max(err / rms, axis=1)
-    print(f"out: max |err|/RMS {rel.max():.4f} (p99 {np.quantile(rel, 0.99):.4f}); "
-          f"rows above {OUT_TOL}: {int(np.sum(rel > OUT_TOL))} of {len(rel)}; "
-          f"max z-flip propagation / RMS {np.max(prop / rms):.4f}", flush=True)
-    assert np.all(err <= OUT_TOL * rms + prop)
+    print(f"out {label}: {len(rel)} rows, max |err|/RMS {rel.max():.5f}, p99.9 {np.quantile(rel, 0.999):.5f}, "
+          f"median {np.median(rel):.5f}; rows above {OUT_TOL}: {int(np.sum(rel > OUT_TOL))}; "
+          f"max z-flip propagation / RMS {np.max(prop / rms):.5f}", flush=True)
+    assert rel.max() <= OUT_TOL, (label, float(rel.max()), int(np.argmax(rel)))
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
@@ -578,7 +574,7 @@ def test_chain_vs_oracle_and_modes_identical(lib, name):
     for m in lib.CHAIN_MODES:
         assert torch.equal(outs[m], outs["chain"]), m
     z_q, z_sf = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="mxfp8")
-    check_out_against_oracle(c, outs["chain"], z_q, z_sf, ref)
+    check_out_against_oracle(c, outs["chain"], z_q, z_sf, ref, name)
 
 
 @pytest.mark.parametrize("M", [1, 7, 33, 129, 300])
@@ -590,7 +586,7 @@ def test_ragged_token_counts(lib, M):
     ref = cr.o_proj_chain_rows(c.x_bits, *c.o_w, rows=rows)
     z_q, z_sf, z_b = lib.grouped_fp8_einsum(x, None, c.wa_q, c.wa_sf, out="both")
     check_z_against_oracle(z_q, z_sf, z_b, ref)
-    check_out_against_oracle(c, out, z_q, z_sf, ref)
+    check_out_against_oracle(c, out, z_q, z_sf, ref, f"ragged M={M}")
     # rows are independent: the first M rows of the 300-row batch agree with the M-row call to within the
     # accumulation order (different token counts take different kernels: 300 rows the tile kernel, up to
     # 32 the whole-K kernel, in between the split-K one)
@@ -614,19 +610,98 @@ def test_outputs_respect_strides_and_guards(lib):
     assert bool((zb[:, G * N:] == 7.0).all())
 
 
+# The chain over the 20 token counts the benchmark sweeps (1-256 decode, 384, 512-32768 prefill), as
+# prefixes of the long configuration's x (BF16 N(0, 1) with 0.1% of entries x100).
+SWEEP_SIZES = (1, 2, 4, 8, 16, 32, 64, 128, 192, 256, 384, 512, 768, 1024, 2048, 4096, 8192, 16384, 24576, 32768)
+
+
+def test_chain_modes_bitwise_identical_at_sweep_sizes(lib):
+    """vLLM PR #60118, Validation: the fused and unfused chains give bitwise identical outputs at every size
+    measured.  At each of the 20 sizes the three arrangements -- standalone quantize + einsum with MXFP8
+    epilogue + GEMM, the einsum on BF16 x (x_fused), and the einsum writing BF16 z re-quantized by a
+    separate launch (unfused) -- give the same output bytes, and the fused z equals the quantizer applied to
+    the same kernel's BF16 z (PR #60118, Tests).  Sixteen sampled rows of each size also meet the output bar
+    against the oracle."""
+    c = get_case("long", lib)
+    rng = np.random.default_rng(60118)
+    for M in SWEEP_SIZES:
+        x = c.x[:M]
+        outs = {m: lib.o_proj_chain(x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode=m) for m in lib.CHAIN_MODES}
+        for m in lib.CHAIN_MODES:
+            assert torch.equal(outs[m], outs["chain"]), (M, m)
+        z_q, z_sf, z_b = lib.grouped_fp8_einsum(x, None, c.wa_q, c.wa_sf, out="both")
+        q2, s2 = lib.mxfp8_quantize(z_b)
+        assert torch.equal(q2, z_q) and torch.equal(s2, z_sf), M
+        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 14), replace=False)]))
+        ref = c.oracle(rows)
+        idx = torch.from_numpy(rows).to(dev())
+        check_out_against_oracle(c, outs["chain"][idx], z_q[idx], z_sf[idx], ref, f"sweep M={M}")
+        del outs, z_q, z_sf, z_b, q2, s2
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [1, 129, 8193])
+def test_fused_z_identity_under_graph_replay(lib, M):
+    """vLLM PR #60118, Tests: at 1, 129 and 8193 tokens, with the einsum and wo_b captured in a HIP graph and
+    replayed, the FP8 data and scales the einsum's epilogue writes are byte-identical to what wo_b's own
+    quantization of the BF16 z gives, and the chain's output equals wo_b run on that BF16 z.  Every replay
+    (three, with eager work between them) equals the eager result."""
+    c = get_case("long", lib)
+    x = c.x[:M].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def body():
+        z_q, z_sf, z_b = lib.grouped_fp8_einsum(x, None, c.wa_q, c.wa_sf, out="both", stream=s)
+        out = lib.fp8_gemm_nt(z_q, z_sf, c.wb_q, c.wb_sf, stream=s)
+        out_b = lib.fp8_gemm_nt(z_b, None, c.wb_q, c.wb_sf, stream=s)      # wo_b quantizing the BF16 z itself
+        q_b, sf_b = lib.mxfp8_quantize(z_b, stream=s)
+        return z_q, z_sf, z_b, out, out_b, q_b, sf_b
+
+    with torch.cuda.stream(s):
+        eager = [t.clone() for t in body()]                # also sizes the stream's workspace before capture
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        static = body()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in static:
+            t.zero_()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        z_q, z_sf, z_b, out, out_b, q_b, sf_b = static
+        assert torch.equal(z_q, q_b) and torch.equal(z_sf, sf_b), (M, rep)
+        assert torch.equal(out, out_b), (M, rep)
+        for a, b in zip(static, eager):
+            assert torch.equal(a, b), (M, rep)
+        lib.o_proj_chain(c.x[:M], c.wa_q, c.wa_sf, c.wb_q, c.wb_sf)     # eager work between replays
+        torch.cuda.synchronize()
+    oq, osf = mx.quantize(to_np(z_b))                          # and the oracle's quantizer agrees
+    assert np.array_equal(to_np(z_q), oq) and np.array_equal(to_np(z_sf), osf)
+    del g
+
+
 @pytest.mark.parametrize("name", ["prefill", "long"])
-def test_large_configs_sampled_rows(lib, name):
+def test_large_configs_against_oracle(lib, name):
+    """Prefill: every one of the 4096 rows against the oracle.  Long: a seeded sample of 2048 rows plus the
+    first and last 128 (the oracle's float64 x for all 32768 rows would take 8.6 GB)."""
     c = get_case(name, lib)
     M = c.shape.M
     out = lib.o_proj_chain(c.x, c.wa_q, c.wa_sf, c.wb_q, c.wb_sf, mode="chain")
     z_q, z_sf, z_b = lib.grouped_fp8_einsum(c.x, None, c.wa_q, c.wa_sf, out="both")
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.choice(M, 128, replace=False)]))
-    print(f"{name}: oracle on {len(rows)} sampled rows of {M}", flush=True)
+    if name == "prefill":
+        rows = np.arange(M)
+    else:
+        rng = np.random.default_rng(20260004)
+        rows = np.unique(np.concatenate([np.arange(128), np.arange(M - 128, M),
+                                         rng.choice(np.arange(128, M - 128), 2048, replace=False)]))
+    print(f"{name}: oracle on {len(rows)} rows of {M}", flush=True)
     ref = c.oracle(rows)
     idx = torch.from_numpy(rows).to(dev())
     check_z_against_oracle(z_q[idx], z_sf[idx], z_b[idx], ref)
-    check_out_against_oracle(c, out[idx], z_q[idx], z_sf[idx], ref)
+    check_out_against_oracle(c, out[idx], z_q[idx], z_sf[idx], ref, name)
     out_oz = lib.fp8_gemm_nt(u8_to_dev(ref.z_q), i32_to_dev(ref.z_sf), c.wb_q, c.wb_sf)
     assert row_rel_err(to_np(out_oz), ref.out64).max() <= OUT_TOL
     # invariants at full size
@@ -757,3 +832,62 @@ def test_graph_survives_workspace_growth(lib):
         torch.cuda.synchronize()
         assert torch.equal(out_static, eager), rep
     assert all(bool((j == 0x7F).all()) for j in junk)
+
+
+def test_capture_on_a_cold_stream_raises(lib):
+    """A split-K call captured on a stream that has no workspace yet raises a clear error instead of capturing
+    a zero fill whose counters would stay undefined until the first replay; after one eager call on the
+    stream the same capture works."""
+    c = get_case("ragged", lib)
+    args = (c.wa_q, c.wa_sf, c.wb_q, c.wb_sf)
+    x_static = c.x[:64].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError, match="workspace"):
+        with torch.cuda.graph(g, stream=s):
+            lib.o_proj_chain(x_static, *args, stream=s)
+    del g
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        eager = lib.o_proj_chain(x_static, *args, stream=s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out = lib.o_proj_chain(x_static, *args, stream=s)
+    with torch.cuda.stream(s):
+        g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
+
+
+def test_outgrown_workspaces_are_released_unless_captured(lib):
+    """Growing a stream's workspace releases the old buffer when no graph captured it, so a sweep of growing
+    shapes holds one buffer per stream; a captured buffer is retained until release_retained_workspaces()."""
+    from mxfp8_activation_quantization_amd import binding as B
+    c = get_case("ragged", lib)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    key = (dev().index or 0, s.cuda_stream)
+    n0 = len(B._retained)
+    with torch.cuda.stream(s):
+        for M in (17, 64, 100, 300):                           # staged BF16 activations: growing workspaces
+            lib.fp8_gemm_nt(c.x[:M, :8192], None, c.wb_q, c.wb_sf, stream=s)
+    s.synchronize()
+    assert len(B._retained) == n0
+    assert B._workspaces[key].numel() >= B.lib().fp8_gemm_nt_workspace_size(B.MXFP8_ACT_BF16, 300, 5120, 8192)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lib.fp8_gemm_nt(c.x[:64, :8192], None, c.wb_q, c.wb_sf, stream=s)
+    torch.cuda.synchronize()
+    big = torch.randn(1024, 8192, device=dev()).to(torch.bfloat16)
+    with torch.cuda.stream(s):
+        lib.fp8_gemm_nt(big, None, c.wb_q, c.wb_sf, stream=s)      # grows past the captured buffer
+    s.synchronize()
+    assert len(B._retained) == n0 + 1
+    with torch.cuda.stream(s):
+        g.replay()
+    torch.cuda.synchronize()
+    del g
+    assert lib.release_retained_workspaces() >= 1
+    assert len(B._retained) == 0
