@@ -78,7 +78,8 @@ typedef enum {
   MXFP8_ERR_ALIAS = 5,        /* an output overlaps an input or another output */
   MXFP8_ERR_DEVICE = 6,       /* the current HIP device is missing or is not gfx950 */
   MXFP8_ERR_LAUNCH = 7,       /* the kernel launch failed */
-  MXFP8_ERR_WORKSPACE = 8     /* workspace missing, too small, or misaligned */
+  MXFP8_ERR_WORKSPACE = 8,    /* workspace missing, too small, or misaligned */
+  MXFP8_ERR_SCRATCH = 9       /* fp8_gemm_nt_noalloc: the shape needs more than its fixed scratch */
 } mxfp8_status;
 
 /* Activation kinds: the type tag of an activation operand.  A producer/consumer
@@ -197,6 +198,36 @@ int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, in
 /* Workspace bytes fp8_gemm_nt needs for this activation kind and shape (0 = none);
  * -1 for an invalid kind or shape. */
 int64_t fp8_gemm_nt_workspace_size(int a_kind, int64_t M, int64_t N, int64_t K);
+
+/*
+ * fp8_gemm_nt_noalloc -- fp8_gemm_nt for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, meaning, kernels and results (bit for bit)
+ * as fp8_gemm_nt, without the workspace arguments: where fp8_gemm_nt needs a
+ * workspace (fp8_gemm_nt_workspace_size > 0: split-K partials of the few-token
+ * kernels, BF16 activations staged as MXFP8), this call uses a fixed device
+ * array of MXFP8_NOALLOC_SCRATCH_BYTES inside the library instead.  It never
+ * calls hipMalloc, hipFree or any allocating routine.
+ *
+ *   - Limit: a shape whose workspace need exceeds MXFP8_NOALLOC_SCRATCH_BYTES
+ *     returns MXFP8_ERR_SCRATCH after the usual argument checks, nothing
+ *     launched (e.g. BF16 activations of more than about 1900 rows at
+ *     K = 8192; MXFP8 activations never stage, and the decode shapes' split-K
+ *     scratch is a few MB).
+ *   - The array is per GPU (each device holds its own copy, from the library's
+ *     load until the process ends) and shared by every call on that GPU: calls
+ *     that overlap in time on one GPU (other streams, other threads, a graph
+ *     replaying while an eager call runs) race on it and must be serialized
+ *     by the caller.  Calls in one stream's order are safe.
+ *   - The first call on a device also enqueues, on its stream and ahead of its
+ *     own kernels, a kernel that zero-fills the split-K counters (the kernels
+ *     leave them at zero after every call, as with a workspace).
+ */
+#define MXFP8_NOALLOC_SCRATCH_BYTES ((int64_t)16 << 20)
+int fp8_gemm_nt_noalloc(int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf,
+                        int64_t M, int64_t N, int64_t K,
+                        const void* b, const int32_t* b_sf,
+                        void* d, int64_t ld_d, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     device_check,
     release_retained_workspaces,
     fp8_gemm_nt,
+    fp8_gemm_nt_noalloc,
     grouped_fp8_einsum,
     lib,
     mxfp8_quantize,

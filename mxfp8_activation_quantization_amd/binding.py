@@ -23,12 +23,13 @@ MXFP8_ERR_ALIAS = 5
 MXFP8_ERR_DEVICE = 6
 MXFP8_ERR_LAUNCH = 7
 MXFP8_ERR_WORKSPACE = 8
+MXFP8_ERR_SCRATCH = 9
 
 MXFP8_ACT_BF16 = 0
 MXFP8_ACT_MXFP8 = 1
 
 _ARG_ERRORS = {MXFP8_ERR_NULL, MXFP8_ERR_SHAPE, MXFP8_ERR_ALIGN, MXFP8_ERR_UNSUPPORTED, MXFP8_ERR_ALIAS,
-               MXFP8_ERR_WORKSPACE}
+               MXFP8_ERR_WORKSPACE, MXFP8_ERR_SCRATCH}
 
 c_i64 = ctypes.c_int64
 c_int = ctypes.c_int
@@ -48,6 +49,8 @@ SIGNATURES = {
     "fp8_gemm_nt": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64,
                             c_vp, c_i64, c_vp]),
     "fp8_gemm_nt_workspace_size": (c_i64, [c_int, c_i64, c_i64, c_i64]),
+    "fp8_gemm_nt_noalloc": (c_int, [c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64,
+                                    c_vp]),
     # include/mxfp8_testing.h: the same calls with the split-K combine chosen per call
     "mxfp8_testing_grouped_fp8_einsum": (c_int, [c_int, c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                                  c_vp, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
@@ -332,6 +335,25 @@ def fp8_gemm_nt(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_s
         _check(_lib.fp8_gemm_nt(*args), "fp8_gemm_nt")
     else:
         _check(_lib.mxfp8_testing_fp8_gemm_nt(SPLITK_MODES[splitk_combine], *args), "mxfp8_testing_fp8_gemm_nt")
+    return d
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20     # MXFP8_NOALLOC_SCRATCH_BYTES
+
+
+def fp8_gemm_nt_noalloc(a: torch.Tensor, a_sf: torch.Tensor | None, b: torch.Tensor, b_sf: torch.Tensor,
+                        d: torch.Tensor, stream=None) -> torch.Tensor:
+    """fp8_gemm_nt without a workspace: the library's fixed per-GPU scratch serves the kernels instead (for
+    callers that cannot allocate; calls that overlap in time on one GPU race on it).  `d` is required."""
+    if b.dim() != 2 or b.dtype != torch.uint8 or b_sf.dtype != torch.int32:
+        raise ValueError("b must be uint8 [N, K] and b_sf int32 [N, K/128]")
+    if not (b.is_contiguous() and b_sf.is_contiguous()):
+        raise ValueError("b and b_sf must be contiguous")
+    N, K = b.shape
+    kind, ap, lda, asfp, ldasf = _act_args(a, a_sf)
+    _rows(d, torch.bfloat16, "d")
+    _check(_lib.fp8_gemm_nt_noalloc(kind, ap, lda, asfp, ldasf, a.shape[0], N, K, _ptr(b), _ptr(b_sf), _ptr(d),
+                                    d.stride(0), _stream(stream)), "fp8_gemm_nt_noalloc")
     return d
 
 

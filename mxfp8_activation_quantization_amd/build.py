@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libmxfp8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "quantize.hip", "rmsnorm_quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "rmsnorm_quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

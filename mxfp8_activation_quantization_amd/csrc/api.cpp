@@ -129,6 +129,7 @@ MX_API const char* mxfp8_status_string(int status) {
     case MXFP8_ERR_DEVICE: return "the current HIP device is missing or is not gfx950";
     case MXFP8_ERR_LAUNCH: return "kernel launch failed";
     case MXFP8_ERR_WORKSPACE: return "workspace missing, too small, or misaligned";
+    case MXFP8_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point's fixed buffer";
     default: return "unknown status";
   }
 }
@@ -246,7 +247,8 @@ namespace mx {
 
 int gemm_entry(int splitk_mode, int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf,
                int64_t M, int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
-               void* workspace, int64_t workspace_bytes, void* stream) {
+               void* workspace, int64_t workspace_bytes, void* stream, ScratchSource scratch,
+               int64_t scratch_bytes) {
   if (splitk_mode < mx::SPLITK_LOCAL || splitk_mode > mx::SPLITK_RECOMPUTE) return MXFP8_ERR_UNSUPPORTED;
   if (M < 0 || K <= 0 || K % 128 || N <= 0 || N % 128) return MXFP8_ERR_SHAPE;
   if (K > kMaxDepth || M > INT32_MAX || N > INT32_MAX) return MXFP8_ERR_SHAPE;
@@ -267,6 +269,14 @@ int gemm_entry(int splitk_mode, int a_kind, const void* a, int64_t ld_a, const i
   p.splitk_mode = splitk_mode;
   Range rw;
   const mx::GemmPlan plan = mx::plan_gemm(M, 1, N, K, a_kind == MXFP8_ACT_BF16);
+  if (scratch && plan.workspace_bytes > 0) {
+    // the caller's fixed scratch array stands in for the workspace (every argument is checked by now)
+    if (plan.workspace_bytes > scratch_bytes) return MXFP8_ERR_SCRATCH;
+    if (const int dc = device_check(); dc != MXFP8_OK) return dc;
+    workspace = scratch(static_cast<hipStream_t>(stream));
+    if (!workspace) return MXFP8_ERR_LAUNCH;
+    workspace_bytes = scratch_bytes;
+  }
   if (int s = bind_workspace(plan, workspace, workspace_bytes, p, rw); s != MXFP8_OK) return s;
   if (overlaps(rw, out)) return MXFP8_ERR_ALIAS;
   for (const Range& in : ins)
@@ -295,7 +305,7 @@ MX_API int fp8_gemm_nt(int a_kind, const void* a, int64_t ld_a, const int32_t* a
                        int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
                        void* workspace, int64_t workspace_bytes, void* stream) {
   return mx::gemm_entry(mx::SPLITK_LOCAL, a_kind, a, ld_a, a_sf, ld_asf, M, N, K, b, b_sf, d, ld_d, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, nullptr, 0);
 }
 
 // Test-only forms (include/mxfp8_testing.h): the same calls with the split-K combine chosen per call.
@@ -313,7 +323,7 @@ MX_API int mxfp8_testing_fp8_gemm_nt(int splitk_combine, int a_kind, const void*
                                      const void* b, const int32_t* b_sf, void* d, int64_t ld_d, void* workspace,
                                      int64_t workspace_bytes, void* stream) {
   return mx::gemm_entry(splitk_combine, a_kind, a, ld_a, a_sf, ld_asf, M, N, K, b, b_sf, d, ld_d, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, nullptr, 0);
 }
 
 MX_API int64_t grouped_fp8_einsum_workspace_size(int x_kind, int64_t M, int64_t G, int64_t K, int64_t N) {

@@ -70,10 +70,15 @@ hipError_t launch_rmsnorm_quantize(const void* x, int64_t M, int64_t K, int64_t 
                                    void* y, int64_t ld_y, void* q, int64_t ld_q, int32_t* sf, int64_t ld_sf,
                                    hipStream_t stream);
 
-// fp8_gemm_nt with every argument check and the split-K combine chosen per call.
+// fp8_gemm_nt with every argument check, the split-K combine chosen per call, and --
+// when `scratch` is given and the plan needs scratch -- the workspace taken from
+// scratch(stream) (at most scratch_bytes, MXFP8_ERR_SCRATCH beyond) instead of the
+// workspace arguments, after the argument checks and the device check.
+using ScratchSource = void* (*)(hipStream_t stream);
 int gemm_entry(int splitk_mode, int a_kind, const void* a, int64_t ld_a, const int32_t* a_sf, int64_t ld_asf,
                int64_t M, int64_t N, int64_t K, const void* b, const int32_t* b_sf, void* d, int64_t ld_d,
-               void* workspace, int64_t workspace_bytes, void* stream);
+               void* workspace, int64_t workspace_bytes, void* stream, ScratchSource scratch,
+               int64_t scratch_bytes);
 
 // out: 1 = BF16 only, 2 = MXFP8 only, 3 = both.  p.ws_* must point into a
 // workspace of at least plan_gemm(...).workspace_bytes when that is non-zero.
