@@ -236,6 +236,7 @@ int einsum_impl(int splitk_mode, int x_kind, const void* x, int64_t ld_x, const 
   p.zq = static_cast<uint8_t*>(z_q); p.ld_zq = ld_z;
   p.zsf = reinterpret_cast<uint8_t*>(z_sf); p.ld_zsf_bytes = ld_zsf * 4;
   p.zb = static_cast<uint16_t*>(z_bf16); p.ld_zb = ld_zb;
+  p.split_act = true;       // the activations carry rare large outliers (see gemm_common.hpp)
   const int out = (want_bf ? 1 : 0) | (want_mx ? 2 : 0);
   const hipError_t e = launch(p, plan, G, x_kind == MXFP8_ACT_BF16, out, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;

@@ -152,7 +152,7 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-template <int MT, int OUT, bool XB>
+template <int MT, int OUT, bool XB, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   static_assert(kRing == 4, "wait_stages covers up to kRing - 2 stages in flight");
@@ -241,8 +241,8 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
           if (j < nsteps) {
             const int sw = (int)(table_word(wtab, rt * 32 + i, j) >> (8 * q));
             const int sx = (int)(table_word(xtab, tt * 32 + i, j) >> (8 * q));
-            acc = mfma_scaled<0>(ring_frag(st.w[h], rt, 0, lane), ring_frag(st.x[h], tt, 0, lane), acc, sw, sx);
-            acc = mfma_scaled<2>(ring_frag(st.w[h], rt, 1, lane), ring_frag(st.x[h], tt, 1, lane), acc, sw, sx);
+            acc = mfma_act<0, SPLIT>(ring_frag(st.w[h], rt, 0, lane), ring_frag(st.x[h], tt, 0, lane), acc, sw, sx);
+            acc = mfma_act<2, SPLIT>(ring_frag(st.w[h], rt, 1, lane), ring_frag(st.x[h], tt, 1, lane), acc, sw, sx);
           }
         }
       }
@@ -519,7 +519,7 @@ __device__ __forceinline__ void gv_wait(int n) {
   }
 }
 
-template <int OUT, int XG>
+template <int OUT, int XG, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
   using C = GvCfg<XG>;
@@ -608,8 +608,8 @@ void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
       if (j < ksteps) {
         const int sw = (int)(gv_table_word(wtab, i, j) >> (8 * q));
         const int sx = (int)(gv_table_word(xtab, xi, j) >> (8 * q));
-        acc = mfma_scaled<0>(gv_frag(st.w[par], i, 0, q), gv_frag(st.x[par], xi, 0, q), acc, sw, sx);
-        acc = mfma_scaled<2>(gv_frag(st.w[par], i, 1, q), gv_frag(st.x[par], xi, 1, q), acc, sw, sx);
+        acc = mfma_act<0, SPLIT>(gv_frag(st.w[par], i, 0, q), gv_frag(st.x[par], xi, 0, q), acc, sw, sx);
+        acc = mfma_act<2, SPLIT>(gv_frag(st.w[par], i, 1, q), gv_frag(st.x[par], xi, 1, q), acc, sw, sx);
       }
     }
   };
@@ -644,7 +644,7 @@ void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
 // table (scale bytes) -- the same bytes the standalone quantizer writes, so the
 // result is the one pre-quantized activations give.  The stage count is a
 // compile-time constant: every register set, load and wait below is static.
-template <int OUT, int XG, int NST>
+template <int OUT, int XG, int NST, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
   using C = GvCfg<XG>;
@@ -784,8 +784,8 @@ void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
     const int j = SS * t + par;
     const int sw = (int)(gv_table_word(wtab, i, j) >> (8 * q));
     const int sx = (int)(gv_table_word(xtab, xi, j) >> (8 * q));
-    acc = mfma_scaled<0>(gv_frag(st.w[par], i, 0, q), gv_frag(st.x[par], xi, 0, q), acc, sw, sx);
-    acc = mfma_scaled<2>(gv_frag(st.w[par], i, 1, q), gv_frag(st.x[par], xi, 1, q), acc, sw, sx);
+    acc = mfma_act<0, SPLIT>(gv_frag(st.w[par], i, 0, q), gv_frag(st.x[par], xi, 0, q), acc, sw, sx);
+    acc = mfma_act<2, SPLIT>(gv_frag(st.w[par], i, 1, q), gv_frag(st.x[par], xi, 1, q), acc, sw, sx);
   });
   wait_vmcnt<0>();                                  // the switched-off weight loads of the last iterations
 
@@ -807,79 +807,70 @@ void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
   }
 }
 
-template <int OUT, int XG>
+template <int OUT, int XG, bool SPLIT>
 static hipError_t launch_whole_k_xb(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
   const dim3 grid((unsigned)plan.workgroups), block(kThreads);
   if (p.K == 32 * 128)
-    hipLaunchKernelGGL((whole_k_xb_kernel<OUT, XG, 32 / GvCfg<XG>::SS>), grid, block, 0, stream, p, (int)G,
+    hipLaunchKernelGGL((whole_k_xb_kernel<OUT, XG, 32 / GvCfg<XG>::SS, SPLIT>), grid, block, 0, stream, p, (int)G,
                        plan.n_tiles);
   else if (p.K == 64 * 128)
-    hipLaunchKernelGGL((whole_k_xb_kernel<OUT, XG, 64 / GvCfg<XG>::SS>), grid, block, 0, stream, p, (int)G,
+    hipLaunchKernelGGL((whole_k_xb_kernel<OUT, XG, 64 / GvCfg<XG>::SS, SPLIT>), grid, block, 0, stream, p, (int)G,
                        plan.n_tiles);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-template <int OUT>
+template <int OUT, bool SPLIT>
 static hipError_t launch_whole_k_bf16(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  if (p.M <= 8) return launch_whole_k_xb<OUT, 1>(p, plan, G, stream);
-  if (p.M <= 16) return launch_whole_k_xb<OUT, 2>(p, plan, G, stream);
+  if (p.M <= 8) return launch_whole_k_xb<OUT, 1, SPLIT>(p, plan, G, stream);
+  if (p.M <= 16) return launch_whole_k_xb<OUT, 2, SPLIT>(p, plan, G, stream);
   return hipErrorInvalidValue;
 }
 
-template <int OUT, int XG>
+template <int OUT, int XG, bool SPLIT>
 static hipError_t launch_whole_k_xg(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  hipLaunchKernelGGL((whole_k_kernel<OUT, XG>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p,
-                     (int)G, plan.n_tiles);
+  hipLaunchKernelGGL((whole_k_kernel<OUT, XG, SPLIT>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream,
+                     p, (int)G, plan.n_tiles);
   return hipGetLastError();
 }
 
-template <int OUT>
+template <int OUT, bool SPLIT>
 static hipError_t launch_whole_k(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  if (p.M <= 8) return launch_whole_k_xg<OUT, 1>(p, plan, G, stream);
-  if (p.M <= 16) return launch_whole_k_xg<OUT, 2>(p, plan, G, stream);
-  if (p.M <= 32) return launch_whole_k_xg<OUT, 4>(p, plan, G, stream);
-  if (p.M <= 64) return launch_whole_k_xg<OUT, 8>(p, plan, G, stream);
-  if (p.M <= 128) return launch_whole_k_xg<OUT, 16>(p, plan, G, stream);
+  if (p.M <= 8) return launch_whole_k_xg<OUT, 1, SPLIT>(p, plan, G, stream);
+  if (p.M <= 16) return launch_whole_k_xg<OUT, 2, SPLIT>(p, plan, G, stream);
+  if (p.M <= 32) return launch_whole_k_xg<OUT, 4, SPLIT>(p, plan, G, stream);
+  if (p.M <= 64) return launch_whole_k_xg<OUT, 8, SPLIT>(p, plan, G, stream);
+  if (p.M <= 128) return launch_whole_k_xg<OUT, 16, SPLIT>(p, plan, G, stream);
   return hipErrorInvalidValue;
 }
 
-template <int MT, int OUT, bool XB>
+template <int MT, int OUT, bool XB, bool SPLIT>
 static hipError_t launch_stream(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  hipLaunchKernelGGL((stream_kernel<MT, OUT, XB>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream, p, (int)G,
-                     plan.n_tiles, plan.chunks, plan.splits);
+  hipLaunchKernelGGL((stream_kernel<MT, OUT, XB, SPLIT>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream,
+                     p, (int)G, plan.n_tiles, plan.chunks, plan.splits);
   return hipGetLastError();
-}
-
-template <int MT>
-static hipError_t dispatch(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,
-                           hipStream_t s) {
-  if (x_bf16) {
-    if (out == OUT_BF16) return launch_stream<MT, OUT_BF16, true>(p, plan, G, s);
-    if (out == OUT_MX) return launch_stream<MT, OUT_MX, true>(p, plan, G, s);
-    return launch_stream<MT, OUT_BOTH, true>(p, plan, G, s);
-  }
-  if (out == OUT_BF16) return launch_stream<MT, OUT_BF16, false>(p, plan, G, s);
-  if (out == OUT_MX) return launch_stream<MT, OUT_MX, false>(p, plan, G, s);
-  return launch_stream<MT, OUT_BOTH, false>(p, plan, G, s);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& p, const GemmPlan& plan, int64_t G, bool x_bf16, int out,
                               hipStream_t stream) {
-  if (plan.whole_k) {
-    if (x_bf16) {
-      if (!plan.whole_k_bf16) return hipErrorInvalidValue;   // the caller quantizes into the workspace first
-      if (out == OUT_BF16) return launch_whole_k_bf16<OUT_BF16>(p, plan, G, stream);
-      if (out == OUT_MX) return launch_whole_k_bf16<OUT_MX>(p, plan, G, stream);
-      return launch_whole_k_bf16<OUT_BOTH>(p, plan, G, stream);
+  return with_variant(p.split_act, out, [&](auto out_tag, auto split_tag) -> hipError_t {
+    constexpr int OUT = decltype(out_tag)::value;
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    if (plan.whole_k) {
+      if (x_bf16) {
+        if (!plan.whole_k_bf16) return hipErrorInvalidValue;   // the caller quantizes into the workspace first
+        return launch_whole_k_bf16<OUT, SPLIT>(p, plan, G, stream);
+      }
+      return launch_whole_k<OUT, SPLIT>(p, plan, G, stream);
     }
-    if (out == OUT_BF16) return launch_whole_k<OUT_BF16>(p, plan, G, stream);
-    if (out == OUT_MX) return launch_whole_k<OUT_MX>(p, plan, G, stream);
-    return launch_whole_k<OUT_BOTH>(p, plan, G, stream);
-  }
-  if (plan.mt == 1) return dispatch<1>(p, plan, G, x_bf16, out, stream);
-  return dispatch<2>(p, plan, G, x_bf16, out, stream);
+    if (plan.mt == 1) {
+      return x_bf16 ? launch_stream<1, OUT, true, SPLIT>(p, plan, G, stream)
+                    : launch_stream<1, OUT, false, SPLIT>(p, plan, G, stream);
+    }
+    return x_bf16 ? launch_stream<2, OUT, true, SPLIT>(p, plan, G, stream)
+                  : launch_stream<2, OUT, false, SPLIT>(p, plan, G, stream);
+  });
 }
 
 }  // namespace mx

@@ -83,7 +83,7 @@ struct DlLds {
 
 // One output tile: weight rows n0 .. n0 + BN - 1 of group g x tokens m0 .. m0 + BM - 1,
 // the whole K range.  `smem` is the workgroup's LDS (at least DlLds<C>::BYTES).
-template <class C, int OUT>
+template <class C, int OUT, bool SPLIT>
 __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g, int64_t n0, int64_t m0) {
   static_assert(C::NW == 4, "four waves");
   constexpr int WI = C::BN / 32;                 // weight load instructions per wave and K-step (8 rows each)
@@ -168,9 +168,11 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     for (int b = 0; b < C::TM; ++b) acc[a][b] = zero16();
 
   // MFMA operands of the two half steps of a K-step, held in registers: f0 (first
-  // half) and f1 (second half).
+  // half) and f1 (second half).  With SPLIT, fx holds an activation fragment's small
+  // codes and fxh its large ones (split once the fragment's read has completed).
   struct Frags {
     v8i fw[C::TN], fx[C::TM];
+    v8i fxh[SPLIT ? C::TM : 1];
     int sw[C::TN], sx[C::TM];
   };
   // The fragment reads are inline assembly with explicit base registers and
@@ -267,24 +269,47 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
   // k = 4s, of scale group s+1 -- switched off (zero-byte resources) where those do
   // not exist -- so the number of loads issued after step k+1's is a constant, and
   // the last step's reads fetch a buffer that is never used.
-  constexpr int NMF = C::TN / 2 * C::TM;             // MFMAs per quarter
-  constexpr auto load_slot = [](int d) constexpr { return d * 3 * NMF / L; };   // MFMA of A2, B1, B2 it follows
-  constexpr int P12 = (2 * L + 2) / 3;               // loads in A2 and B1: load_slot(d) < 2 NMF <=> 3d < 2L
+  // With SPLIT every (weight tile, token tile) pair takes two MFMAs, one per part of the
+  // activation fragment: a quarter issues all its small-code MFMAs, then all its large-code
+  // ones (no two consecutive MFMAs on one accumulator), and the first quarter of each half
+  // step splits each activation fragment just ahead of its first MFMA, so the bit operations
+  // overlap the MFMAs already in the pipeline.
+  constexpr int NMF = C::TN / 2 * C::TM;             // (weight tile, token tile) pairs per quarter
+  constexpr int NM = SPLIT ? 2 * NMF : NMF;          // MFMA slots per quarter
+  constexpr auto load_slot = [](int d) constexpr { return d * 3 * NM / L; };   // MFMA of A2, B1, B2 it follows
+  constexpr int P12 = (2 * L + 2) / 3;               // loads in A2 and B1: load_slot(d) < 2 NM <=> 3d < 2L
   Frags f0, f1;
   auto mfma_q = [&](auto j_tag, auto quarter_tag, int k) {
     constexpr int J = decltype(j_tag)::value, Q = decltype(quarter_tag)::value;   // Q: 0 = A1 .. 3 = B2
     constexpr int H = Q / 2;
     Frags& F = H == 0 ? f0 : f1;
     const bool on = k + C::NB < ksteps;
-    static_for<NMF>([&](auto m_tag) {
+    // SPLIT: f1's activation fragments (read in A1) are split during A2, which multiplies f0;
+    // f0's for the next step (read in B1) during B2, which multiplies f1, once their reads
+    // are done -- so the bit operations overlap MFMAs on other registers.
+    constexpr int SPLIT_EVERY = NM / C::TM;           // MFMA slots between two fragment splits
+    if constexpr (SPLIT && Q == 3) {
+      asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(3 * (C::TN - 1)));   // all but the late weight tiles
+      tie_x(f0);
+      shift_scales(f0, 0, 0, true);
+    }
+    static_for<NM>([&](auto m_tag) {
       constexpr int m = decltype(m_tag)::value;
-      constexpr int a = (Q % 2) * (C::TN / 2) + m / C::TM, b = m % C::TM;
-      acc[a][b] = mfma_scaled<2 * H>(F.fw[a], F.fx[b], acc[a][b], F.sw[a], F.sx[b]);
+      constexpr int mm = m % NMF;
+      constexpr int a = (Q % 2) * (C::TN / 2) + mm / C::TM, b = mm % C::TM;
+      if constexpr (m < NMF)
+        acc[a][b] = mfma_scaled<2 * H>(F.fw[a], F.fx[b], acc[a][b], F.sw[a], F.sx[b]);
+      else
+        acc[a][b] = mfma_scaled<2 * H>(F.fw[a], F.fxh[b], acc[a][b], F.sw[a], F.sx[b]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (Q == 0 || Q == 3) {
+      if constexpr (SPLIT && (Q == 1 || Q == 3) && m % SPLIT_EVERY == SPLIT_EVERY - 1) {
+        Frags& S = Q == 1 ? f1 : f0;
+        split_large_codes(S.fx[m / SPLIT_EVERY], S.fxh[m / SPLIT_EVERY]);
+      }
+      if constexpr (Q == 0 || Q == (SPLIT ? 2 : 3)) {
         static_for<NT>([&](auto t_tag) {
           constexpr int t = decltype(t_tag)::value;
-          if constexpr (t * NMF / NT == m) {
+          if constexpr (t * NM / NT == m) {
             if constexpr (Q == 0)
               read_tile(std::integral_constant<int, order(t)>{}, j_tag, std::integral_constant<int, 1>{}, f1);
             else
@@ -296,7 +321,7 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
       if constexpr (Q > 0) {
         static_for<L>([&](auto d_tag) {
           constexpr int d = decltype(d_tag)::value;
-          if constexpr (load_slot(d) == (Q - 1) * NMF + m)
+          if constexpr (load_slot(d) == (Q - 1) * NM + m)
             issue_one(d_tag, std::integral_constant<int, J % C::NB>{}, k + C::NB, on);
         });
       }
@@ -324,6 +349,33 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     mfma_q(j_tag, std::integral_constant<int, 3>{}, k);
   };
 
+  // SPLIT: the barrier that publishes step k+1 comes before B1 (one quarter earlier), so that B1
+  // can read f0 of step k+1 and B2 split it; the loads outstanding at that wait are those of
+  // steps k+2 .. k+NB-1, A2's of this step, and the scale groups as above.
+  constexpr int P1 = (L + 2) / 3;                    // loads in A2: load_slot(d) < NM <=> 3d < L
+  auto kstep_split = [&](auto j_tag, int k) {
+    constexpr int J = decltype(j_tag)::value;
+    asm volatile("s_waitcnt lgkmcnt(0)");          // f0's weight tiles, read in the previous step's B1
+    tie_w(f0, 0, C::TN);
+    shift_scales(f0, 0, C::TN, false);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(j_tag, std::integral_constant<int, 0>{}, k);
+    asm volatile("s_waitcnt lgkmcnt(0)");          // f1, read in A1
+    tie_w(f1, 0, C::TN);
+    tie_x(f1);
+    shift_scales(f1, 0, C::TN, true);
+    asm volatile("s_barrier" ::: "memory");
+    if constexpr (J % 4 == 0)
+      issue_scales(std::integral_constant<int, (J / 4 + 1) % 2>{}, k / 4 + 1, 4 * (k / 4 + 1) < ksteps);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(j_tag, std::integral_constant<int, 1>{}, k);
+    wait_vmcnt<(C::NB - 2) * L + P1 + (J % 4 <= C::NB - 2 ? SI : 0)>();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(j_tag, std::integral_constant<int, 2>{}, k);
+    mfma_q(j_tag, std::integral_constant<int, 3>{}, k);
+  };
+
   issue_scales(std::integral_constant<int, 0>{}, 0, true);
   static_for<C::NB>([&](auto b_tag) {
     constexpr int b = decltype(b_tag)::value;
@@ -335,10 +387,20 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     read_tile(std::integral_constant<int, order(decltype(t_tag)::value)>{}, std::integral_constant<int, 0>{},
               std::integral_constant<int, 0>{}, f0);
   });
+  if constexpr (SPLIT) {
+    asm volatile("s_waitcnt lgkmcnt(0)");
+    tie_x(f0);
+    shift_scales(f0, 0, 0, true);
+#pragma unroll
+    for (int c = 0; c < C::TM; ++c) split_large_codes(f0.fx[c], f0.fxh[c]);
+  }
   for (int k0 = 0; k0 < ksteps; k0 += 8) {
     static_for<8>([&](auto j_tag) {
       constexpr int J = decltype(j_tag)::value;
-      if (J == 0 || k0 + J < ksteps) kstep(j_tag, k0 + J);
+      if (J == 0 || k0 + J < ksteps) {
+        if constexpr (SPLIT) kstep_split(j_tag, k0 + J);
+        else kstep(j_tag, k0 + J);
+      }
     });
   }
   // The last step's reads of f0 (of a step that does not exist; f1's reads were
@@ -403,7 +465,7 @@ __device__ __forceinline__ void panel_tile(int wi, int nf, int R, int PW, int& g
   nt = panel * PW + k % w;
 }
 
-template <class CF, class CT, int OUT>
+template <class CF, class CT, int OUT, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dl_gemm_kernel(GemmArgs p, int G, int full_rows, int rows) {
   static_assert(CF::BM == CT::BM, "rows of BM tokens");
@@ -415,27 +477,27 @@ void dl_gemm_kernel(GemmArgs p, int G, int full_rows, int rows) {
   if ((int)blockIdx.x < F) {
     int g, nt, mt;
     panel_tile(xcd_work_index((int)blockIdx.x, F), nf, full_rows, 4, g, nt, mt);
-    dl_tile<CF, OUT>(p, smem, g, (int64_t)nt * CF::BN, (int64_t)mt * BM);
+    dl_tile<CF, OUT, SPLIT>(p, smem, g, (int64_t)nt * CF::BN, (int64_t)mt * BM);
   } else {
     const int tr = rows - full_rows;
     int g, nt, mt;
     panel_tile(xcd_work_index((int)blockIdx.x - F, G * ntl * tr), ntl, tr, 8, g, nt, mt);
-    dl_tile<CT, OUT>(p, smem, g, (int64_t)nt * CT::BN, (int64_t)(full_rows + mt) * BM);
+    dl_tile<CT, OUT, SPLIT>(p, smem, g, (int64_t)nt * CT::BN, (int64_t)(full_rows + mt) * BM);
   }
 }
 
-template <class CF, class CT, int OUT>
+template <class CF, class CT, int OUT, bool SPLIT>
 static hipError_t launch_dl(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  hipLaunchKernelGGL((dl_gemm_kernel<CF, CT, OUT>), dim3((unsigned)plan.workgroups), dim3(256), 0, stream, p, (int)G,
-                     plan.full_rows, plan.rows);
+  hipLaunchKernelGGL((dl_gemm_kernel<CF, CT, OUT, SPLIT>), dim3((unsigned)plan.workgroups), dim3(256), 0, stream, p,
+                     (int)G, plan.full_rows, plan.rows);
   return hipGetLastError();
 }
 
 template <class CF, class CT>
 static hipError_t dispatch_out(const GemmArgs& p, const GemmPlan& plan, int64_t G, int out, hipStream_t s) {
-  if (out == OUT_BF16) return launch_dl<CF, CT, OUT_BF16>(p, plan, G, s);
-  if (out == OUT_MX) return launch_dl<CF, CT, OUT_MX>(p, plan, G, s);
-  return launch_dl<CF, CT, OUT_BOTH>(p, plan, G, s);
+  return with_variant(p.split_act, out, [&](auto out_tag, auto split_tag) -> hipError_t {
+    return launch_dl<CF, CT, decltype(out_tag)::value, decltype(split_tag)::value>(p, plan, G, s);
+  });
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& p, const GemmPlan& plan, int64_t G, int out, hipStream_t stream) {

@@ -32,6 +32,7 @@ struct GemmArgs {
   uint32_t* ws_counters;  // split-K arrival counters (zero between calls), or null
   float* ws_partials;     // split-K fp32 partial tiles, or null
   int splitk_mode;        // how split-K partials are combined (SplitKMode)
+  bool split_act;         // feed the activation codes >= 0x68 and the rest as two MFMA operands (the einsum)
 };
 
 enum TileCfg { TILE_BIG = 0, TILE_MID = 1 };

@@ -17,10 +17,12 @@ The shapes are the DeepSeek-V4.1-Flash TP1 o_proj of vLLM PR #60118
     RMS (max |err| / RMS);
   * the whole chain: max |out - out64| / RMS(row) <= 2e-2 on every row checked
     (the bar as stated, no allowance).  The propagation through |wo_b| of the z
-    code flips that the z bar admits is printed beside it as a diagnostic:
-    gfx950's FP8 MFMA aligns the products of one dot product to the largest
-    with about twelve fractional bits, so a few BF16 z values land one rounding
-    step away from the float64 value and flip a code by one ulp.
+    code flips that the z bar admits is printed beside it as a diagnostic.
+    (gfx950's FP8 MFMA cuts each product of a group of 8 to 13 bits below the
+    group's largest; the einsum feeds large and small activation codes as two
+    operands so that x's outliers do not cost their neighbours bits -- see
+    test_gpu_mfma_precision.py -- which keeps the chain's error at that of
+    rounding the exact result to BF16.)
 """
 import numpy as np
 import pytest
