@@ -47,16 +47,24 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
 // and the chain's output error falls to that of rounding the exact result to BF16.
 constexpr uint32_t kSplitBias = 0x80u - 0x68u;   // per byte: (|code| + bias) has bit 7 set iff |code| >= 0x68
 
+// Dword D of a fragment: its codes of magnitude >= 0x68 into hi (others zero), the rest stay in lo.
+template <int D>
+__device__ __forceinline__ void split_large_dword(v8i& lo, v8i& hi) {
+  const uint32_t u = (uint32_t)lo[D];
+  // bit 7 of each byte of t: |code| >= 0x68 ((0x80 | c) - 0x68 borrows from no other byte)
+  const uint32_t t = (u | 0x80808080u) - (0x80u - kSplitBias) * 0x01010101u;
+  // v_perm_b32 selectors 8-11 give 0xFF or 0x00 from bit 7 of bytes 1, 3, 5, 7 of {src0, src1}:
+  // with src1 = t and src0 = t << 8 those are t's bytes 1, 3, 0, 2
+  const uint32_t mask = __builtin_amdgcn_perm(t << 8, t, 0x090B080Au);
+  hi[D] = (int)(u & mask);
+  lo[D] = (int)(u ^ (u & mask));
+}
+
 // The codes of magnitude >= 0x68 of a fragment (others zero) and the remaining codes (those zero).
 __device__ __forceinline__ void split_large_codes(v8i& lo, v8i& hi) {
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    const uint32_t u = (uint32_t)lo[d];
-    const uint32_t m = ((u & 0x7F7F7F7Fu) + kSplitBias * 0x01010101u) & 0x80808080u;   // no carry between bytes
-    const uint32_t mask = m | (m - (m >> 7));                                             // 0x80 -> 0xFF per byte
-    hi[d] = (int)(u & mask);
-    lo[d] = (int)(u & ~mask);
-  }
+  split_large_dword<0>(lo, hi); split_large_dword<1>(lo, hi); split_large_dword<2>(lo, hi);
+  split_large_dword<3>(lo, hi); split_large_dword<4>(lo, hi); split_large_dword<5>(lo, hi);
+  split_large_dword<6>(lo, hi); split_large_dword<7>(lo, hi);
 }
 
 // acc + W . X with the activation operand X split as above when SPLIT (the small codes first, then the
@@ -163,7 +171,7 @@ template <int OUT, int TN>
 __device__ __forceinline__ void epi_store_rows(const GemmArgs& p, const uint8_t* chunk, int64_t m_base, int64_t nb,
                                                int lane) {
   constexpr int RS = EpiLds<TN>::RS;
-  static_assert(TN == 1 || TN == 2 || TN == 4, "lane split of a row");
+  static_assert(TN == 1 || TN == 2 || TN == 4 || TN == 8, "lane split of a row");
   if constexpr (OUT & OUT_BF16) {
     constexpr int LPR = 4 * TN, RPP = 64 / LPR;      // lanes per row (8 columns each), rows per pass
 #pragma unroll

@@ -216,6 +216,8 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     if (k <= C::TM) return C::TN + k - 1;                   // X0 .. X(TM-1)
     return k - C::TM;                                       // W1 .. W(TN-1)
   };
+  // SPLIT reads a half step's activation tiles first: B2 splits them while the weight reads finish
+  constexpr auto order_split = [](int k) constexpr { return k < C::TM ? C::TN + k : k - C::TM; };
   static_assert(C::TN % 2 == 0, "weight tiles split evenly over the two halves of a half step");
   constexpr int LATE_LDS_OPS = 3 * (C::TN / 2);             // scale word + two halves per late tile
   auto shift_scales = [&](Frags& F, int a0, int a1, bool x) {
@@ -287,9 +289,14 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
     // SPLIT: f1's activation fragments (read in A1) are split during A2, which multiplies f0;
     // f0's for the next step (read in B1) during B2, which multiplies f1, once their reads
     // are done -- so the bit operations overlap MFMAs on other registers.
-    constexpr int SPLIT_EVERY = NM / C::TM;           // MFMA slots between two fragment splits
+    // the TM fragments' 8 TM dwords spread evenly over the quarter's NM slots (in-order issue: a burst of
+    // bit operations after one MFMA would hold back the next MFMA's issue while the pipe drains)
+    constexpr int SPLIT_DW = 8 * C::TM;
+    constexpr int SPLIT_PER_SLOT = (SPLIT_DW + NM - 1) / NM;
     if constexpr (SPLIT && Q == 3) {
-      asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(3 * (C::TN - 1)));   // all but the late weight tiles
+      // B1 read the activation tiles first (order_split): at most the weight tiles' reads may
+      // still be in flight (the counter holds 15 at most; waiting for more is only earlier)
+      asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(3 * C::TN < 15 ? 3 * C::TN : 15));
       tie_x(f0);
       shift_scales(f0, 0, 0, true);
     }
@@ -302,9 +309,12 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
       else
         acc[a][b] = mfma_scaled<2 * H>(F.fw[a], F.fxh[b], acc[a][b], F.sw[a], F.sx[b]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (SPLIT && (Q == 1 || Q == 3) && m % SPLIT_EVERY == SPLIT_EVERY - 1) {
+      if constexpr (SPLIT && (Q == 1 || Q == 3)) {
         Frags& S = Q == 1 ? f1 : f0;
-        split_large_codes(S.fx[m / SPLIT_EVERY], S.fxh[m / SPLIT_EVERY]);
+        static_for<SPLIT_PER_SLOT>([&](auto j_tag) {
+          constexpr int w = m * SPLIT_PER_SLOT + decltype(j_tag)::value;
+          if constexpr (w < SPLIT_DW) split_large_dword<w % 8>(S.fx[w / 8], S.fxh[w / 8]);
+        });
       }
       if constexpr (Q == 0 || Q == (SPLIT ? 2 : 3)) {
         static_for<NT>([&](auto t_tag) {
@@ -312,6 +322,9 @@ __device__ __forceinline__ void dl_tile(const GemmArgs& p, uint8_t* smem, int g,
           if constexpr (t * NM / NT == m) {
             if constexpr (Q == 0)
               read_tile(std::integral_constant<int, order(t)>{}, j_tag, std::integral_constant<int, 1>{}, f1);
+            else if constexpr (SPLIT)
+              read_tile(std::integral_constant<int, order_split(t)>{}, std::integral_constant<int, (J + 1) % 8>{},
+                        std::integral_constant<int, 0>{}, f0);
             else
               read_tile(std::integral_constant<int, order(t)>{}, std::integral_constant<int, (J + 1) % 8>{},
                         std::integral_constant<int, 0>{}, f0);
