@@ -20,7 +20,7 @@
         consecutive quantize -> einsum -> gemm triple, with the launches and gaps.
 
 Kernels are told apart by name and output mode (the streaming kernel's second
-template argument, the whole-K kernel's first, the tile kernel's last: 1 = BF16
+template argument, the whole-K kernel's first, the tile kernel's third: 1 = BF16
 out: fp8_gemm_nt, 2 = MXFP8 out: grouped_fp8_einsum); the quantize kernel is
 mxfp8_quantize.  Only the grid that occurs most often is kept for
 each, which drops the one-off launches of the set-up (weight quantization).
@@ -64,7 +64,7 @@ def template_args(n: str):
 
 def chain_role(name: str):
     """quantize / einsum (MXFP8 out) / gemm (BF16 out) from a kernel name: the output mode is the
-    second template argument of the streaming kernel, the first of the whole-K kernels and the last
+    second template argument of the streaming kernel, the first of the whole-K kernels and the third
     of the tile kernel."""
     n = short_name(name)
     if n.startswith("quantize_kernel"):
@@ -77,8 +77,8 @@ def chain_role(name: str):
         out = args[1]
     elif kern in ("whole_k_kernel", "whole_k_xb_kernel"):
         out = args[0]
-    elif kern == "dl_gemm_kernel":
-        out = args[-1]
+    elif kern == "dl_gemm_kernel" and len(args) >= 3:
+        out = args[2]
     else:
         return None
     return {"1": "gemm", "2": "einsum", "3": "einsum"}.get(out)
