@@ -437,6 +437,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="run the configuration's shapes, seed and outlier rate at this many tokens instead (the "
+                         "workload is then named CONFIG_M<tokens>, e.g. for kernel traces and counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--arms", default="chain,x_fused,unfused")
     ap.add_argument("--sweep", default=DEFAULT_SWEEP,
@@ -473,9 +476,15 @@ def main():
     L.device_check()
     cfg = si.CHAIN_CONFIGS[args.config]
     S = cfg.shape
+    wname = args.config
+    if args.tokens is not None:
+        if args.tokens < 1:
+            raise SystemExit("--tokens must be at least 1")
+        S = si.ChainShape(args.tokens, S.G, S.K, S.N, S.P)
+        wname = f"{args.config}_M{args.tokens}"
     M, G, K, N, P = S.M, S.G, S.K, S.N, S.P
     dev = torch.device("cuda", 0)
-    print(f"[bench] config {args.config}: M={M} G={G} K={K} N={N} P={P}; generating inputs", file=sys.stderr,
+    print(f"[bench] config {wname}: M={M} G={G} K={K} N={N} P={P}; generating inputs", file=sys.stderr,
           flush=True)
     inp = si.chain_inputs(S, cfg.seed, cfg.outlier_rate)
 
@@ -584,7 +593,7 @@ def main():
 
     dom = max(("einsum", "gemm"), key=lambda k: t_k[k])
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
     if os.path.exists(tpath):
         with open(tpath) as f:
             tr = json.load(f)
@@ -596,7 +605,7 @@ def main():
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp8 (e4m3 x e4m3, fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": f"{args.config}: o_proj chain (mxfp8_quantize -> grouped_fp8_einsum with MXFP8 "
+        "config": {"workload": f"{wname}: o_proj chain (mxfp8_quantize -> grouped_fp8_einsum with MXFP8 "
                                f"epilogue -> fp8_gemm_nt), M={M} tokens, wo_a {G}x{K}->{N}, wo_b {G * N}->{P}",
                    "M": M, "G": G, "K": K, "N": N, "P": P, "seed": cfg.seed,
                    "x": "BF16 N(0,1)" + (f", {cfg.outlier_rate:g} of entries x100" if cfg.outlier_rate else ""),
@@ -624,7 +633,7 @@ def main():
         line["quant_sweep"] = quant_sweep(torch, L, si, stream, args)
     if args.producer_sweep:
         line["producer_sweep"] = producer_sweep(torch, L, si, stream, args)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.tokens is None:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.config, inp)
     if args.cpu_long:

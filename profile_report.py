@@ -127,8 +127,16 @@ def main_grid(d, role):
 
 def cmd_traffic(a):
     sys.path.insert(0, ROOT)
-    from bench import kernel_source_hash
+    from bench import chain_bytes, kernel_source_hash
+    import synth_inputs as si
 
+    # the workload's shapes: a chain configuration, or one run at another token count (NAME_M<tokens>)
+    base, _, tok = a.config.partition("_M")
+    shape = si.CHAIN_CONFIGS[base].shape if base in si.CHAIN_CONFIGS else None
+    algo = {}
+    if shape is not None:
+        M = int(tok) if tok else shape.M
+        algo = chain_bytes(M, shape.G, shape.K, shape.N, shape.P)
     res = {"config": a.config, "kernel_source_hash": kernel_source_hash(), "commands": a.command or []}
     cal = {}
     for counter, path in (("FETCH_SIZE", a.copy_fetch), ("WRITE_SIZE", a.copy_write)):
@@ -146,8 +154,9 @@ def cmd_traffic(a):
     lines.append("")
     lines.append(f"Calibration: a device copy of {a.copy_bytes} bytes reads as FETCH_SIZE x "
                  f"{cal['FETCH_SIZE']:.3f} and WRITE_SIZE x {cal['WRITE_SIZE']:.3f} bytes.\n")
-    lines.append("| launch | grid | dispatches | FETCH bytes | WRITE bytes | HBM bytes per launch |")
-    lines.append("|---|---|---|---|---|---|")
+    lines.append("| launch | grid | dispatches | FETCH bytes | WRITE bytes | HBM bytes per launch | algorithmic bytes "
+                 "| ratio |")
+    lines.append("|---|---|---|---|---|---|---|---|")
     fetch, _ = read_counter(a.fetch, "FETCH_SIZE")
     write, _ = read_counter(a.write, "WRITE_SIZE")
     for role in ("quantize", "einsum", "gemm"):
@@ -159,7 +168,12 @@ def cmd_traffic(a):
         wb = sum(vw) / len(vw) * 1024 * cal["WRITE_SIZE"]
         res[role] = {"grid": gf, "dispatches": len(vf), "fetch_bytes": fb, "write_bytes": wb,
                      "hbm_bytes_per_launch": fb + wb}
-        lines.append(f"| {role} | {gf} | {len(vf)} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} |")
+        if role in algo:
+            res[role]["algorithmic_bytes"] = algo[role]
+            extra = f" {algo[role]:.4g} | {(fb + wb) / algo[role]:.2f} |"
+        else:
+            extra = " | |"
+        lines.append(f"| {role} | {gf} | {len(vf)} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} |" + extra)
     path = os.path.join(ROOT, "profiles", f"traffic_{a.config}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
