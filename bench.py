@@ -52,7 +52,8 @@ ROTATE_BYTES = 600 << 20
 RAMP_S = 0.3          # untimed load before each timed arm (clock ramp-up)
 # token counts of the chain sweep: decode (1-256), 384, and prefill (512-32768)
 DEFAULT_SWEEP = "1,2,4,8,16,32,64,128,192,256,384,512,768,1024,2048,4096,8192,16384,24576,32768"
-KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_skinny.hip", "gemm_common.hpp", "quantize.hip", "mx_device.hpp"]
+KERNEL_SOURCES = ["gemm_tiled.hip", "gemm_tiled.hpp", "gemm_tiled_kernel.hpp", "gemm_tiled_inst.hip", "gemm_skinny.hip",
+                  "gemm_common.hpp", "quantize.hip", "mx_device.hpp"]
 KERNEL_NAMES = {"quantize": "mxfp8_quantize", "einsum": "grouped_fp8_einsum", "gemm": "fp8_gemm_nt"}
 
 

@@ -25,6 +25,9 @@ LIB_NAME = "libmxfp8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["api.cpp", "quantize.hip", "rmsnorm_quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "noalloc.hip"]
+# Sources compiled once per instance (macro = 0 .. count - 1), one object each: the tile kernel's
+# launcher instances, which are the slowest to compile, build in parallel.
+INSTANCED = {"gemm_tiled_inst.hip": ("TILE_INST", 12)}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -78,10 +81,13 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
     cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    units = [(src, os.path.splitext(src)[0], []) for src in SOURCES]
+    for src, (macro, count) in INSTANCED.items():
+        units += [(src, f"{os.path.splitext(src)[0]}_{i}", [f"-D{macro}={i}"]) for i in range(count)]
+    for src, stem, defs in units:
+        obj = os.path.join(BUILD_DIR, stem + ".o")
         lang = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
-        cmds.append([cc, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMMON_FLAGS, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 1)) as ex:
         for cmd, _ in zip(cmds, ex.map(_run, cmds)):
