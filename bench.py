@@ -141,6 +141,9 @@ def cpu_long(block=1024):
     t0 = time.perf_counter()
     for r0 in range(0, M, block):
         cr.o_proj_chain(x[r0:r0 + block], *w)
+        if (r0 + block) % 4096 == 0:
+            print(f"[bench] oracle long: {r0 + block} of {M} rows, {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+                  flush=True)
     el = time.perf_counter() - t0
     flop = cfg.shape.flop
     return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": threads_used(), "kind": "oracle",
