@@ -223,6 +223,19 @@ def median_rounds(torch, graphs_by_arm, stream, reps, rounds=3, ramp_s=RAMP_S, c
     return {a: {"us": float(np.median(v)), "rounds": v, "spread": max(v) - min(v)} for a, v in res.items()}
 
 
+def recorded_traffic(workload, kind):
+    """HBM bytes per launch of `kind` from profiles/traffic_<workload>.json (rocprofv3 FETCH_SIZE +
+    WRITE_SIZE, scaled by a device copy), or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return tr.get(kind, {}).get("hbm_bytes_per_launch")
+
+
 def roofline_block(kind, M, G, K, N, P, t_us, traffic=None):
     """Roofline of one launch (the einsum or the GEMM) at M tokens from its average duration."""
     flops = chain_flops(M, G, K, N, P)[kind]
@@ -293,7 +306,11 @@ def sweep(torch, L, Ms, dims, w, stream, args, kernel_ms=(4096, 32768)):
         res["fusion_saving_us"] = res["unfused_us"] - us
         if M in kernel_ms:
             res["kernels_avg_us"] = kernel_times(torch, L, sets, M, stream, args)
-            res["roofline"] = {k: roofline_block(k, M, G, K, N, P, res["kernels_avg_us"][KERNEL_NAMES[k]])
+            # traffic: the counters of the configuration with this token count (the prefill and long
+            # configurations; same shapes and outlier rate, other seeds)
+            wl = {4096: "prefill", 32768: "long"}.get(M)
+            res["roofline"] = {k: roofline_block(k, M, G, K, N, P, res["kernels_avg_us"][KERNEL_NAMES[k]],
+                                                 recorded_traffic(wl, k) if wl else None)
                                for k in ("einsum", "gemm")}
         print(f"[bench] sweep M={M}: chain {us:.2f} us (spread {res['chain_spread_us']:.2f}), x_fused "
               f"{res['x_fused_us']:.2f} us, unfused {res['unfused_us']:.2f} us, {res['tflops']:.1f} TFLOP/s",
@@ -596,14 +613,7 @@ def main():
     value = total_flop / (us * 1e-6) / 1e12
 
     dom = max(("einsum", "gemm"), key=lambda k: t_k[k])
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
-    if os.path.exists(tpath):
-        with open(tpath) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash():
-            traffic = tr.get(dom, {}).get("hbm_bytes_per_launch")
-    roof = roofline_block(dom, M, G, K, N, P, t_k[dom], traffic)
+    roof = roofline_block(dom, M, G, K, N, P, t_k[dom], recorded_traffic(wname, dom))
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
