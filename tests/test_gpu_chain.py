@@ -670,6 +670,7 @@ def test_fused_z_identity_under_graph_replay(lib, M):
     for rep in range(3):
         for t in static:
             t.zero_()
+        s.wait_stream(torch.cuda.current_stream())         # the fills come before the replay
         with torch.cuda.stream(s):
             g.replay()
         torch.cuda.synchronize()
@@ -784,6 +785,7 @@ def test_graph_replays_equal_eager(lib, M, mode):
     torch.cuda.synchronize()
     for rep in range(3):
         out_static.fill_(7.0)
+        s.wait_stream(torch.cuda.current_stream())         # the fill comes before the replay
         with torch.cuda.stream(s):
             g.replay()
         torch.cuda.synchronize()
@@ -791,6 +793,7 @@ def test_graph_replays_equal_eager(lib, M, mode):
         assert torch.equal(lib.o_proj_chain(other, *args, mode=mode), eager_other), (M, mode, rep)
         torch.cuda.synchronize()
     x_static.copy_(other)
+    s.wait_stream(torch.cuda.current_stream())             # the new input is in place before the replay
     with torch.cuda.stream(s):
         g.replay()
     torch.cuda.synchronize()
@@ -822,6 +825,7 @@ def test_graph_survives_workspace_growth(lib):
     torch.cuda.synchronize()
     # a BF16 GEMM with many tokens stages its activations in the workspace: more bytes than split-K needs
     big = torch.randn(2048, 8192, device=dev()).to(torch.bfloat16)
+    s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         lib.fp8_gemm_nt(big, None, c.wb_q, c.wb_sf, stream=s)
     s.synchronize()
@@ -829,6 +833,7 @@ def test_graph_survives_workspace_growth(lib):
     junk = [torch.full((1 << 20,), 0x7F, dtype=torch.uint8, device=dev()) for _ in range(16)]
     for rep in range(2):
         out_static.fill_(7.0)
+        s.wait_stream(torch.cuda.current_stream())         # the fill comes before the replay
         with torch.cuda.stream(s):
             g.replay()
         torch.cuda.synchronize()
@@ -883,6 +888,7 @@ def test_outgrown_workspaces_are_released_unless_captured(lib):
         lib.fp8_gemm_nt(c.x[:64, :8192], None, c.wb_q, c.wb_sf, stream=s)
     torch.cuda.synchronize()
     big = torch.randn(1024, 8192, device=dev()).to(torch.bfloat16)
+    s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         lib.fp8_gemm_nt(big, None, c.wb_q, c.wb_sf, stream=s)      # grows past the captured buffer
     s.synchronize()

@@ -107,6 +107,7 @@ def test_noalloc_under_graph_capture_on_a_fresh_stream(B):
     torch.cuda.synchronize()
     for rep in range(3):
         d.fill_(7.0)
+        s.wait_stream(torch.cuda.current_stream())         # the fill comes before the replay
         with torch.cuda.stream(s):
             g.replay()
         torch.cuda.synchronize()
