@@ -126,6 +126,22 @@ constexpr int kMaxSteps = 32;
 
 __device__ __forceinline__ int g8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
+// K-steps of the splits: split s of S covers [split_begin(s), split_begin(s + 1)).  When it still fits
+// the scale tables, the last split takes about kSplitSkew steps more than the others, so that it
+// usually finishes after they have published their partials and skips publishing its own (the
+// combine below); otherwise the splits are equal.  Measured (wo_b 8192 -> 5120, 3 splits of 64
+// steps): 20/20/24 saves 0.5-0.7 us per call at 33-64 tokens against 21/21/22; 21/21/22 with the
+// early counter read and 19/19/26 save nothing.
+constexpr int kSplitSkew = 4;
+__device__ __forceinline__ bool split_skewed(int S, int ksteps) {
+  const int b = (ksteps - kSplitSkew) / S;
+  return S > 1 && b >= 1 && ksteps - (S - 1) * b <= kMaxSteps;
+}
+__device__ __forceinline__ int split_begin(int s, int S, int ksteps) {
+  if (s >= S) return ksteps;
+  return split_skewed(S, ksteps) ? s * ((ksteps - kSplitSkew) / S) : (int)((int64_t)s * ksteps / S);
+}
+
 __device__ __forceinline__ v8i ring_frag(const uint8_t* op, int T, int KS, int lane) {
   const int i = lane & 31, q = lane >> 5, r = 32 * T + i, g = g8(r);
   const uint8_t* b = op + 128 * r;
@@ -217,9 +233,9 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   // The K range of split s_ through the pipeline, into a fresh accumulator.  All
   // threads take part (loads and barriers); waves that own no token tile return zeros.
   auto run_split = [&](int s_) -> v16f {
-    const int k_lo = (int)((int64_t)s_ * ksteps / S);
-    const int k_hi = (int)((int64_t)(s_ + 1) * ksteps / S);
-    const int nsteps = k_hi - k_lo;               // <= kMaxSteps (the plan guarantees it)
+    const int k_lo = split_begin(s_, S, ksteps);
+    const int k_hi = split_begin(s_ + 1, S, ksteps);
+    const int nsteps = k_hi - k_lo;               // <= kMaxSteps (the plan and split_skewed guarantee it)
     const int nst = (nsteps + kStageSteps - 1) / kStageSteps;
     __syncthreads();                              // LDS of a previous run is no longer read
 
@@ -401,29 +417,50 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
       p.ws_partials + (int64_t)tc * S * TILE_FLOATS, 0, S * TILE_BYTES, kRsrcFlags);
   const int my_off = ((rt * MT + tt) * 64 + lane) * 64;     // bytes within a split's tile
-  if (computes) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const v4i v = {__float_as_int(acc[4 * k]), __float_as_int(acc[4 * k + 1]), __float_as_int(acc[4 * k + 2]),
-                     __float_as_int(acc[4 * k + 3])};
-      __builtin_amdgcn_raw_buffer_store_b128(v, rp, s * TILE_BYTES + my_off + 16 * k, 0, kL2);
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   unsigned long long* cnt = reinterpret_cast<unsigned long long*>(p.ws_counters) + tc;
-  if (tid == 0) {
-    unsigned xcc;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    xcc &= 7;
-    const unsigned long long old =
-        __hip_atomic_fetch_add(cnt, 1ull | (1ull << (32 + 4 * xcc)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    const bool last = (unsigned)old == (unsigned)(S - 1);
-    const bool here = ((old >> (32 + 4 * xcc)) & 15ull) == (unsigned long long)(S - 1) &&
-                      p.splitk_mode != SPLITK_RECOMPUTE;
-    s_last = (last ? 1 : 0) | (here ? 2 : 0);
+  // The longer last split of a skewed split first reads the counter: when every other split has
+  // arrived it is the last arriver and keeps its partial in registers (the counter is not
+  // incremented, so no other split can take the combine).  Otherwise it takes the usual path.
+  bool kept = false;
+  if (s == S - 1 && split_skewed(S, ksteps)) {
+    if (tid == 0) {
+      unsigned xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      xcc &= 7;
+      const unsigned long long cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const bool all_in = (unsigned)cur == (unsigned)(S - 1);
+      const bool here = ((cur >> (32 + 4 * xcc)) & 15ull) == (unsigned long long)(S - 1) &&
+                        p.splitk_mode != SPLITK_RECOMPUTE;
+      s_last = all_in ? (1 | (here ? 2 : 0)) : 0;
+    }
+    __syncthreads();
+    kept = s_last != 0;
+    __syncthreads();                                // every thread has read s_last before it is written again
   }
-  __syncthreads();
+  if (!kept) {
+    if (computes) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const v4i v = {__float_as_int(acc[4 * k]), __float_as_int(acc[4 * k + 1]), __float_as_int(acc[4 * k + 2]),
+                       __float_as_int(acc[4 * k + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rp, s * TILE_BYTES + my_off + 16 * k, 0, kL2);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      unsigned xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      xcc &= 7;
+      const unsigned long long old =
+          __hip_atomic_fetch_add(cnt, 1ull | (1ull << (32 + 4 * xcc)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const bool last = (unsigned)old == (unsigned)(S - 1);
+      const bool here = ((old >> (32 + 4 * xcc)) & 15ull) == (unsigned long long)(S - 1) &&
+                        p.splitk_mode != SPLITK_RECOMPUTE;
+      s_last = (last ? 1 : 0) | (here ? 2 : 0);
+    }
+    __syncthreads();
+  }
   const int fl = s_last;
   if (!(fl & 1)) return;
   v16f tot = zero16();
