@@ -103,29 +103,29 @@ __device__ __forceinline__ v16f zero16() {
 template <int OUT>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f& acc, int64_t m, bool live, int64_t nb,
                                            int q) {
-  uint32_t h[16];
+  uint32_t h2[8];                                    // BF16 pairs (r, r + 1), r even
 #pragma unroll
-  for (int r = 0; r < 16; ++r) h[r] = bf16_rne(acc[r]);
+  for (int r = 0; r < 16; r += 2) h2[r / 2] = bf16x2_rne(acc[r], acc[r + 1]);
   if constexpr (OUT & OUT_BF16) {
     if (live) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const uint2 v = make_uint2(h[4 * r4] | (h[4 * r4 + 1] << 16), h[4 * r4 + 2] | (h[4 * r4 + 3] << 16));
-        *reinterpret_cast<uint2*>(p.zb + m * p.ld_zb + nb + 8 * r4 + 4 * q) = v;
+        *reinterpret_cast<uint2*>(p.zb + m * p.ld_zb + nb + 8 * r4 + 4 * q) = make_uint2(h2[2 * r4], h2[2 * r4 + 1]);
       }
     }
   }
   if constexpr (OUT & OUT_MX) {
-    uint32_t am = 0;
+    uint32_t am2 = 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) am = max(am, h[r] & 0x7FFFu);
+    for (int k = 0; k < 8; ++k) am2 = amax_pair(am2, h2[k]);
+    uint32_t am = fold_pair(am2);
     am = max(am, (uint32_t)__shfl_xor((int)am, 32));
     const int e = scale_exp_from_amax(am);
     const float scale = exp2_int(e);
     if (live) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const uint32_t c = encode4(h[4 * r4] | (h[4 * r4 + 1] << 16), h[4 * r4 + 2] | (h[4 * r4 + 3] << 16), scale);
+        const uint32_t c = encode4(h2[2 * r4], h2[2 * r4 + 1], scale);
         *reinterpret_cast<uint32_t*>(p.zq + m * p.ld_zq + nb + 8 * r4 + 4 * q) = c;
       }
       if (q == 0) p.zsf[m * p.ld_zsf_bytes + nb / 32] = (uint8_t)(e + 127);
@@ -158,8 +158,7 @@ template <int TN>
 __device__ __forceinline__ void epi_write_tile(uint8_t* chunk, const v16f& acc, int a, int i, int q) {
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) {
-    const uint2 v = make_uint2(bf16_rne(acc[4 * r4]) | (bf16_rne(acc[4 * r4 + 1]) << 16),
-                               bf16_rne(acc[4 * r4 + 2]) | (bf16_rne(acc[4 * r4 + 3]) << 16));
+    const uint2 v = make_uint2(bf16x2_rne(acc[4 * r4], acc[4 * r4 + 1]), bf16x2_rne(acc[4 * r4 + 2], acc[4 * r4 + 3]));
     *reinterpret_cast<uint2*>(chunk + i * EpiLds<TN>::RS + (a * 32 + 8 * r4 + 4 * q) * 2) = v;
   }
 }

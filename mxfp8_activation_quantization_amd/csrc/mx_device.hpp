@@ -60,10 +60,14 @@ __device__ __forceinline__ uint32_t encode4(uint32_t p01, uint32_t p23, float sc
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// fp32 -> BF16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two BF16 values packed in a word (a in the low half), round to nearest even,
+// with gfx950's packed conversion (v_cvt_pk_bf16_f32): one instruction instead of about seven for
+// the integer formula (u + 0x7FFF + bit 16 of u) >> 16, which it matches on every finite fp32 bit
+// pattern, subnormals and overflow to infinity included (checked on the device exhaustively).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
 }
 
 }  // namespace mx

@@ -121,9 +121,7 @@ __global__ __launch_bounds__(kRmsThreads) void rmsnorm_quantize_kernel(
     uint32_t yw[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = bf16_rne((bf16_lo(v[k]) * r) * bf16_lo(g[k]));
-      const uint32_t hi = bf16_rne((bf16_hi(v[k]) * r) * bf16_hi(g[k]));
-      yw[k] = lo | (hi << 16);
+      yw[k] = bf16x2_rne((bf16_lo(v[k]) * r) * bf16_lo(g[k]), (bf16_hi(v[k]) * r) * bf16_hi(g[k]));
     }
     rms_store_span(yw, j, yrow, qrow, sfrow, s);
   };
