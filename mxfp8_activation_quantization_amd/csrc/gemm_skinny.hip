@@ -126,16 +126,18 @@ constexpr int kMaxSteps = 32;
 
 __device__ __forceinline__ int g8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-// K-steps of the splits: split s of S covers [split_begin(s), split_begin(s + 1)).  When it still fits
-// the scale tables, the last split takes about kSplitSkew steps more than the others, so that it
-// usually finishes after they have published their partials and skips publishing its own (the
-// combine below); otherwise the splits are equal.  Measured (wo_b 8192 -> 5120, 3 splits of 64
-// steps): 20/20/24 saves 0.5-0.7 us per call at 33-64 tokens against 21/21/22; 21/21/22 with the
-// early counter read and 19/19/26 save nothing.
+// K-steps of the splits: split s of S covers [split_begin(s), split_begin(s + 1)).  With two or
+// three splits, when it still fits the scale tables, the last split takes about kSplitSkew steps
+// more than the others, so that it usually finishes after they have published their partials and
+// skips publishing its own (the combine below); otherwise the splits are equal.  Measured at 64
+// tokens, alternated on one box: wo_b 8192 -> 5120 (3 splits of 64 steps) 20/20/24 saves 0.5-0.7 us
+// per call against 21/21/22, where 21/21/22 with the early counter read and 19/19/26 save nothing;
+// N = 5120 at K = 2048 / 4096 (3 splits) saves 0.6 / 0.4 us, N = 6144 at K = 4096 (2 splits) 0.8 us;
+// with 4 or 8 splits (N = 4096, K = 4096; N = 2048, K = 8192) the longer last split cost 1.5 / 0.3 us.
 constexpr int kSplitSkew = 4;
 __device__ __forceinline__ bool split_skewed(int S, int ksteps) {
   const int b = (ksteps - kSplitSkew) / S;
-  return S > 1 && b >= 1 && ksteps - (S - 1) * b <= kMaxSteps;
+  return S > 1 && S <= 3 && b >= 1 && ksteps - (S - 1) * b <= kMaxSteps;
 }
 __device__ __forceinline__ int split_begin(int s, int S, int ksteps) {
   if (s >= S) return ksteps;

@@ -294,11 +294,14 @@ def test_split_k_workspace_counters_return_to_zero(lib):
 
 @pytest.mark.parametrize("kind,M,G,N,K", [("gemm", 48, 1, 256, 4096), ("gemm", 64, 1, 5120, 8192),
                                           ("gemm", 5, 1, 128, 2176), ("einsum", 64, 4, 1024, 4096),
-                                          ("einsum", 33, 3, 256, 1024)])
+                                          ("einsum", 33, 3, 256, 1024), ("gemm", 64, 1, 6144, 4096),
+                                          ("gemm", 40, 1, 5120, 2048), ("gemm", 64, 1, 4096, 4096)])
 def test_split_k_combine_modes_give_identical_bits(lib, kind, M, G, N, K):
     """The decode kernels combine split-K partials through one XCD's L2 (default), through memory, or by
     recomputing the other splits (the fallback when a tile's splits ran on different XCDs): all three give
-    the same bits, equal to the oracle in the exact regime, and leave the counters at zero."""
+    the same bits, equal to the oracle in the exact regime, and leave the counters at zero.  The shapes
+    take 2, 3, 4 and 8 splits; with 2 or 3 the last split is the longer one (wo_b: 20/20/24 of 64 steps;
+    6144 x 4096: 14/18; 5120 x 2048: 4/4/8; the 33-token einsum: 2/6), with 4 or 8 they are equal."""
     from mxfp8_activation_quantization_amd import binding as B
     rng = np.random.default_rng(300 + M + N)
     aq, asf = exact_operands(rng, M, G * K)
