@@ -18,7 +18,9 @@
 namespace mx {
 
 constexpr int kQuantThreads = 256;
-constexpr int64_t kQuantMaxBlocks = 256 * 32;   // enough resident waves to cover HBM latency; the rest loops
+// Grid cap: enough resident waves to cover HBM latency; the rest loops.  Measured (BF16 [4096 | 16384,
+// 32768]): 256 x 64 blocks 63.4 / 266 us against 64.6 / 274 for 256 x 32.
+constexpr int64_t kQuantMaxBlocks = 256 * 64;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
