@@ -105,6 +105,26 @@ def test_strided_rows_leave_padding_untouched(lib):
     assert np.all(to_np(q)[:, K:] == 0xA5) and np.all(to_np(sf)[:, K // 128:] == 0x5A5A5A5A)
 
 
+def test_rows_past_one_grid_trip(lib):
+    """More 128-element spans than one trip of the capped grid covers (256 x 64 workgroups x 16 span
+    groups x 4 spans = 2^20 spans = 4096 rows of 32768): the kernel loops, and rows of both trips --
+    the first and last rows, rows at the trip boundary and random rows -- are bit-exact against the
+    oracle.  Rows are independent random finite BF16 patterns, so a row written to the wrong place
+    cannot match by accident."""
+    M, K = 4608, 32768
+    rng = np.random.default_rng(4608)
+    bits = rng.integers(0, 1 << 16, size=(M, K), dtype=np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] &= 0xBFFF                     # no Inf / NaN patterns: clear an exponent bit
+    print(f"quantize grid loop M={M} K={K}", flush=True)
+    q, sf = lib.mxfp8_quantize(bf16_to_dev(bits))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(4090, 4102), np.arange(M - 4, M),
+                                     rng.choice(M, 96, replace=False)]))
+    oq, os_ = mx.quantize(bits[rows])
+    idx = torch.from_numpy(rows).to(dev())
+    assert np.array_equal(to_np(q[idx]), oq) and np.array_equal(to_np(sf[idx]), os_)
+
+
 def test_empty_batch_is_noop(lib):
     x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev())
     q, sf = lib.mxfp8_quantize(x)
