@@ -16,7 +16,10 @@ static hipError_t dispatch_out(const GemmArgs& p, const GemmPlan& plan, int64_t 
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& p, const GemmPlan& plan, int64_t G, int out, hipStream_t stream) {
-  if (plan.tile_cfg == TILE_MID) return dispatch_out<Mid128, Mid64>(p, plan, G, out, stream);   // N % 128 == 0
+  if (plan.tile_cfg == TILE_MID) {                     // N % 128 == 0
+    if (p.split_act) return dispatch_out<Mid128s, Mid64>(p, plan, G, out, stream);
+    return dispatch_out<Mid128, Mid64>(p, plan, G, out, stream);
+  }
   if (p.N % 256 == 0) {
     if (p.split_act) return dispatch_out<Cfg256s, Cfg128>(p, plan, G, out, stream);
     return dispatch_out<Cfg256, Cfg128>(p, plan, G, out, stream);

@@ -29,8 +29,12 @@ using Cfg128 = BigCfg<128, 256, 1, 4>;      // 128 x 64 per wave
 using Mid128 = BigCfg<128, 128, 2, 2, 4>;   // 64 x 64 per wave
 using Mid64 = BigCfg<64, 128, 1, 4, 4>;     // 64 x 32 per wave
 // Split activations (the einsum): 256 x 256 tiles as 1 x 4 waves of 256 x 64, so that each wave splits
-// two activation fragments per half step instead of four (the same bits as the 2 x 2 waves).
+// two activation fragments per half step instead of four (the same bits as the 2 x 2 waves); likewise
+// 128 x 128 tiles as 1 x 4 waves of 128 x 32 (one fragment per half step instead of two).  Measured,
+// alternated on one box: einsum at 4096 tokens 202.5 -> 194.2 us, at 384 / 512 tokens 32.2 / 34.9 ->
+// 29.1 / 32.0 us.
 using Cfg256s = BigCfg<256, 256, 1, 4>;     // 256 x 64 per wave
+using Mid128s = BigCfg<128, 128, 1, 4, 4>;  // 128 x 32 per wave
 
 // Launches the tile kernel for the plan: CF tiles for the first plan.full_rows rows of tokens, CT
 // tiles for the rest.

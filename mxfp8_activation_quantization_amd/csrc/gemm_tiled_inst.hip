@@ -32,11 +32,11 @@ MX_TILE_INSTANCE(Cfg128, Cfg128, OUT_BOTH, true);
 #elif TILE_INST == 8
 MX_TILE_INSTANCE(Mid128, Mid64, OUT_BF16, false);
 #elif TILE_INST == 9
-MX_TILE_INSTANCE(Mid128, Mid64, OUT_BF16, true);
+MX_TILE_INSTANCE(Mid128s, Mid64, OUT_BF16, true);
 #elif TILE_INST == 10
-MX_TILE_INSTANCE(Mid128, Mid64, OUT_MX, true);
+MX_TILE_INSTANCE(Mid128s, Mid64, OUT_MX, true);
 #elif TILE_INST == 11
-MX_TILE_INSTANCE(Mid128, Mid64, OUT_BOTH, true);
+MX_TILE_INSTANCE(Mid128s, Mid64, OUT_BOTH, true);
 #else
 #error "TILE_INST out of range"
 #endif
