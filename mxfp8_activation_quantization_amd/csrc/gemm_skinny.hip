@@ -102,11 +102,13 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, const v16f& acc, 
 //
 // E4M3 activations: both operands are codes, so every byte goes from memory straight into LDS
 // (buffer_load ... lds) and the pipeline depth is bounded by LDS, not registers:
-// a ring of kRing stages of kStageSteps 128-deep steps (64 weight rows and 64 token
-// rows x 128 bytes per step: 32 KB per stage), with the loads of stage t + kRing - 1
-// issued while stage t is multiplied.  One workgroup per CU keeps 48 KB of weights
-// in flight per CU, enough to cover HBM latency at full bandwidth; two steps per
-// stage halve the barriers and the LDS-read -> MFMA latency each stage exposes.  The scale words of the whole K range (up
+// a ring of kRingE4 stages of kStageSteps 128-deep steps (64 weight rows and 64 token
+// rows x 128 bytes per step: 32 KB per stage), with the loads of stage t + kRingE4 - 1
+// issued while stage t is multiplied.  One workgroup per CU keeps 32 KB of weights
+// in flight per CU: with every CU streaming at once, fewer bytes in flight per CU
+// finish sooner (wo_b 8192 -> 5120 at 64 tokens: 15.2 us with two stages in flight,
+// 15.5 with three, alternated on one box); two steps per stage halve the barriers and
+// the LDS-read -> MFMA latency each stage exposes.  The scale words of the whole K range (up
 // to kMaxSteps steps) are fetched once, at the start, into two tables: per step
 // they would be 64 scattered 4-byte reads per operand.
 //
@@ -118,9 +120,10 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, const v16f& acc, 
 // of steps k_lo .. k_lo + 31 as eight 16-byte chunks, chunk c at position c ^ (r & 7).
 // A lane's fragment is row i, chunks 4KS + q and 4KS + 2 + q.  BF16 activations
 // take the same path with the activation slot of each stage filled by the
-// workgroup's own threads (quantized in registers), so E4M3 and BF16 activations
-// give identical bits.
+// workgroup's own threads (quantized in registers, two stages ahead: a ring of
+// kRing stages), so E4M3 and BF16 activations give identical bits.
 constexpr int kRing = 4;
+constexpr int kRingE4 = 3;
 constexpr int kStageSteps = 2;
 constexpr int kMaxSteps = 32;
 
@@ -173,7 +176,7 @@ __device__ __forceinline__ void wait_stages(int n) {
 template <int MT, int OUT, bool XB, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
-  static_assert(kRing == 4, "wait_stages covers up to kRing - 2 stages in flight");
+  static_assert(kRing == 4 && kRingE4 >= 2 && kRingE4 <= kRing, "wait_stages covers up to 2 stages in flight");
   constexpr int L = 4 * kStageSteps;     // load instructions per wave and stage: per step 2 weight, 2 activation
   __shared__ __attribute__((aligned(1024))) RingStage ring[kRing];
   __shared__ __attribute__((aligned(1024))) uint32_t wtab[64 * kMaxSteps];
@@ -250,9 +253,9 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
     }
 
     // multiplies stage t (all threads call it; waves without a token tile skip)
-    auto mma_stage = [&](int t, v16f& acc) {
+    auto mma_stage = [&](int t, v16f& acc, int ring_len) {
       if (computes) {
-        const RingStage& st = ring[t % kRing];
+        const RingStage& st = ring[t % ring_len];
 #pragma unroll
         for (int h = 0; h < kStageSteps; ++h) {
           const int j = kStageSteps * t + h;
@@ -346,7 +349,7 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
         if (t + 2 < nst) quantize_x(X, t + 2);
         issue_w(t + 3);
         load_x(X, t + 4);
-        mma_stage(t, acc);
+        mma_stage(t, acc, kRing);
       };
       for (int t = 0; t < nst; t += 2) {
         step(A, t, t == 0);
@@ -366,7 +369,7 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
     // A stage's second step past the range (odd step count) loads the last step
     // again -- valid addresses -- and is not multiplied.
     auto issue = [&](int t) {
-      RingStage& st = ring[t % kRing];
+      RingStage& st = ring[t % kRingE4];
 #pragma unroll
       for (int h = 0; h < kStageSteps; ++h) {
         const int kk = k_lo + kStageSteps * t + h, k = kk < k_hi ? kk : k_hi - 1;
@@ -380,15 +383,15 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
     };
 
     v16f acc = zero16();
-    const int pre = nst < kRing - 1 ? nst : kRing - 1;
+    const int pre = nst < kRingE4 - 1 ? nst : kRingE4 - 1;
     for (int t = 0; t < pre; ++t) issue(t);
     for (int t = 0; t < nst; ++t) {
       // stage t's loads are done when at most the later issued stages remain in flight
-      const int later = (nst - 1 - t) < (kRing - 2) ? (nst - 1 - t) : (kRing - 2);
+      const int later = (nst - 1 - t) < (kRingE4 - 2) ? (nst - 1 - t) : (kRingE4 - 2);
       wait_stages<L>(later);
       asm volatile("s_barrier" ::: "memory");       // every wave's loads of stage t landed; stage t-1 is free
-      if (t + kRing - 1 < nst) issue(t + kRing - 1);
-      mma_stage(t, acc);
+      if (t + kRingE4 - 1 < nst) issue(t + kRingE4 - 1);
+      mma_stage(t, acc, kRingE4);
     }
     return acc;
   };
