@@ -507,18 +507,19 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
 // token tile tt.  At the end the partial tiles of a token tile are added in wave
 // order through LDS and the first wave of the tile stores it.
 //
-// Ring: kGvStages stages of SS steps (SS = the waves per token tile, so every
-// wave multiplies one step of every stage); per step 32 weight rows and 8 XG token
+// Ring: NS stages of SS steps (SS = the waves per token tile, so every wave
+// multiplies one step of every stage); per step 32 weight rows and 8 XG token
 // rows x 128 bytes (XG = 1, 2, 4, 8 or 16 groups of 8 token rows, the fewest that
 // hold M), the slot layout of the streaming kernel above.  The ring is shallow on
 // purpose: with every CU streaming at once, deeper rings (8 to 12 stages of two
-// steps were measured) finished later, and four stages of four steps (48 KB of
-// weights in flight per CU) were fastest at both wo_a and wo_b shapes.  Token
+// steps were measured) finished later; kGvStages = 4 stages, or 3 where up to 32
+// tokens run on a grid that holds every CU (the launcher below).  Token
 // rows past M arrive as zeros or are not loaded at all; MFMA lanes of tokens past
 // the loaded rows read a loaded row again.  Those output columns are never
 // stored.  Scale tables for up to kGvMaxSteps steps are fetched once, at the start.
 constexpr int kGvMaxSteps = 64;
 constexpr int kGvStages = 4;
+constexpr int64_t kWholeKShallowMinWorkgroups = 256;
 
 template <int XG>
 struct GvCfg {
@@ -561,11 +562,11 @@ __device__ __forceinline__ void gv_wait(int n) {
   }
 }
 
-template <int OUT, int XG, bool SPLIT>
+template <int OUT, int XG, int NS, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void whole_k_kernel(GemmArgs p, int G, int n_tiles) {
   using C = GvCfg<XG>;
-  constexpr int NS = kGvStages, SS = C::SS, XR = C::XR;
+  constexpr int SS = C::SS, XR = C::XR;
   static_assert(NS >= 3 && SS * (1 + C::XI) * (NS - 2) <= 63, "ring depth within the vmcnt range");
   __shared__ __attribute__((aligned(1024))) GvStage<XG> ring[NS];
   __shared__ __attribute__((aligned(1024))) uint32_t wtab[32 * kGvMaxSteps];
@@ -872,8 +873,16 @@ static hipError_t launch_whole_k_bf16(const GemmArgs& p, const GemmPlan& plan, i
 
 template <int OUT, int XG, bool SPLIT>
 static hipError_t launch_whole_k_xg(const GemmArgs& p, const GemmPlan& plan, int64_t G, hipStream_t stream) {
-  hipLaunchKernelGGL((whole_k_kernel<OUT, XG, SPLIT>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0, stream,
-                     p, (int)G, plan.n_tiles);
+  // Ring depth: with up to 32 tokens on a grid that holds every CU, three stages (two in flight)
+  // instead of four.  Measured, alternated on one box: einsum 8 x 4096 -> 1024 (256 workgroups) at
+  // 8 / 20 / 32 tokens 9.18 / 9.27 / 9.55 -> 8.55 / 8.89 / 9.21 us; wo_b 8192 -> 5120 (160 workgroups)
+  // 10.95 / 12.1 -> 11.44 / 12.35 us with three, so smaller grids keep four.
+  if (XG <= 4 && plan.workgroups >= kWholeKShallowMinWorkgroups)
+    hipLaunchKernelGGL((whole_k_kernel<OUT, XG, 3, SPLIT>), dim3((unsigned)plan.workgroups), dim3(kThreads), 0,
+                       stream, p, (int)G, plan.n_tiles);
+  else
+    hipLaunchKernelGGL((whole_k_kernel<OUT, XG, kGvStages, SPLIT>), dim3((unsigned)plan.workgroups), dim3(kThreads),
+                       0, stream, p, (int)G, plan.n_tiles);
   return hipGetLastError();
 }
 

@@ -158,12 +158,13 @@ def test_tile_families_give_identical_bits(lib, kind, M_small, M_big, G, N, K):
 
 @pytest.mark.parametrize("M", [1, 7, 12, 32])
 @pytest.mark.parametrize("kind,G,N,K", [("gemm", 1, 4096, 8192), ("gemm", 1, 5120, 384), ("einsum", 8, 512, 256),
-                                        ("einsum", 4, 1024, 1152)])
+                                        ("einsum", 4, 1024, 1152), ("einsum", 8, 1024, 2048), ("gemm", 1, 8192, 1152)])
 def test_whole_k_exact_regime_bitexact(lib, kind, M, G, N, K):
     """At most 32 tokens with at least 128 workgroups of 32 weight rows: each workgroup takes the whole K
     range (up to 64 steps of 128, odd step counts included) and its four waves' partial tiles are added at
-    the end; the ring holds 8, 16 or 32 token rows per step (M = 1, 7 | 12 | 32).  Bit-exact in the exact
-    regime, for every output form."""
+    the end; the ring holds 8, 16 or 32 token rows per step (M = 1, 7 | 12 | 32), four stages deep on grids
+    of 128-160 workgroups and three on grids of 256 (the last two shapes).  Bit-exact in the exact regime,
+    for every output form."""
     rng = np.random.default_rng(7000 + M + K)
     aq, asf = exact_operands(rng, M, G * K)
     wq, wsf = exact_operands(rng, G * N, K)
