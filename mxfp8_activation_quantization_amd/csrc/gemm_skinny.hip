@@ -513,12 +513,16 @@ void stream_kernel(GemmArgs p, int G, int n_tiles, int chunks, int S) {
 // hold M), the slot layout of the streaming kernel above.  The ring is shallow on
 // purpose: with every CU streaming at once, deeper rings (8 to 12 stages of two
 // steps were measured) finished later; kGvStages = 4 stages, or 3 where up to 32
-// tokens run on a grid that holds every CU (the launcher below).  Token
+// tokens run on a grid that holds every CU (the launcher below), and kXbStages = 3
+// for the BF16-activation variant at up to 16 tokens (0.7 to 0.8 us less than 4 on
+// the 256-workgroup wo_a einsum at 1 to 16 tokens, 0.2 us less on the 8192 -> 5120
+// GEMM, equal on 32- and 64-tile grids).  Token
 // rows past M arrive as zeros or are not loaded at all; MFMA lanes of tokens past
 // the loaded rows read a loaded row again.  Those output columns are never
 // stored.  Scale tables for up to kGvMaxSteps steps are fetched once, at the start.
 constexpr int kGvMaxSteps = 64;
 constexpr int kGvStages = 4;
+constexpr int kXbStages = 3;
 constexpr int64_t kWholeKShallowMinWorkgroups = 256;
 
 template <int XG>
@@ -692,7 +696,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
   using C = GvCfg<XG>;
   static_assert(XG <= 2, "at most 16 tokens");
-  constexpr int NS = kGvStages, SS = C::SS, XR = C::XR;
+  constexpr int NS = kXbStages, SS = C::SS, XR = C::XR;
+  static_assert(NS >= 3, "weights of stage t+NS-1 go into the slot stage t-1 freed");
   constexpr int KSTEPS = SS * NST;
   static_assert(KSTEPS <= kGvMaxSteps, "scale tables hold kGvMaxSteps steps");
   constexpr int BLK = SS * XR * 4;                 // activation blocks per stage
@@ -794,9 +799,8 @@ void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
   XRegs A, B;
   load_x(A, 0);
   load_x(B, 1);
-  issue_w(0);
-  issue_w(1);
-  issue_w(2);
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) issue_w(t);
   wait_vmcnt<0>();
 #pragma unroll
   for (int u = 0; u < 4 * BPT; ++u) {
@@ -807,9 +811,11 @@ void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
   quantize_x(B, 1);
   load_x(A, 2);
   load_x(B, 3);
-  // iteration t: the registers of stage t+2 (set t % 2) are complete once only the
-  // previous iteration's batch (SS weight loads, and 4 BPT activation loads while
-  // stage t+3 exists) is in flight.  Activation loads past the last stage are not
+  // iteration t: the weights of stage t (issued NS-1 iterations earlier) and the
+  // registers of stage t+2 (set t % 2) are complete once only the previous
+  // iteration's batch (SS weight loads, and 4 BPT activation loads while stage t+3
+  // exists) is in flight.  Both writes of stage t+2 and the weights of stage
+  // t+NS-1 go into slots that stage t-1 or earlier freed.  Activation loads past the last stage are not
   // issued at all: a load whose registers the compiler takes as dead would still
   // write them when it returns.
   static_for<NST>([&](auto t_tag) {
@@ -821,7 +827,7 @@ void whole_k_xb_kernel(GemmArgs p, int G, int n_tiles) {
     for (int u = 0; u < 4 * BPT; ++u) tie_after_wait(X.v[u]);
     lds_barrier();                                  // stage t landed and quantized everywhere; t-1 is free
     if constexpr (t + 2 < NST) quantize_x(X, t + 2);
-    issue_w(t + 3);
+    issue_w(t + NS - 1);
     if constexpr (t + 4 < NST) load_x(X, t + 4);
     const GvStage<XG>& st = ring[t % NS];
     const int j = SS * t + par;
