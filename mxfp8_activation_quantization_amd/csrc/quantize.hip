@@ -21,6 +21,8 @@ constexpr int kQuantThreads = 256;
 // Grid cap: enough resident waves to cover HBM latency; the rest loops.  Measured (BF16 [4096 | 16384,
 // 32768]): 256 x 64 blocks 63.4 / 266 us against 64.6 / 274 for 256 x 32.
 constexpr int64_t kQuantMaxBlocks = 256 * 64;
+// Grids of two spans per trip below this many blocks (half of the 256 CUs) take one span per trip.
+constexpr int64_t kQuantNarrowBelow = 128;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -78,15 +80,24 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, int64_t ld_x, vo
   const int64_t spans_per_row = K / 128;
   const int64_t total = M * spans_per_row;
   const int64_t per_block = kQuantThreads / 16;
-  // two spans per trip while that fills the grid; four once the grid is at its cap
+  // two spans per trip while that fills the grid; four once the grid is at its cap; one
+  // while two would leave more than half the CUs without a workgroup.  Measured (BF16
+  // [M, 32768], alternated on one box): one span per trip at 1 / 8 tokens 2.75 / 2.67 us
+  // against 2.82 / 3.10 with two, but 3.9 / 4.6 / 6.9 against 3.6 / 4.3 / 6.3 at 64 / 128 / 256
+  // tokens; four spans per trip were slower at every size up to 256 tokens.
   const int64_t blocks2 = (total + 2 * per_block - 1) / (2 * per_block);
   const bool wide = blocks2 > kQuantMaxBlocks;
-  int64_t blocks = wide ? (total + 4 * per_block - 1) / (4 * per_block) : blocks2;
+  const bool narrow = blocks2 < kQuantNarrowBelow;
+  int64_t blocks = wide ? (total + 4 * per_block - 1) / (4 * per_block)
+                        : (narrow ? (total + per_block - 1) / per_block : blocks2);
   if (blocks > kQuantMaxBlocks) blocks = kQuantMaxBlocks;
   if (blocks < 1) blocks = 1;
   auto* xp = static_cast<const uint16_t*>(x);
   auto* qp = static_cast<uint8_t*>(q);
-  if (wide)
+  if (narrow)
+    hipLaunchKernelGGL(quantize_kernel<1>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, xp, ld_x, qp, ld_q,
+                       sf, ld_sf, spans_per_row, total);
+  else if (wide)
     hipLaunchKernelGGL(quantize_kernel<4>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, xp, ld_x, qp, ld_q,
                        sf, ld_sf, spans_per_row, total);
   else
