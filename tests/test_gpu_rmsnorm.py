@@ -72,6 +72,23 @@ def test_large_batch_sampled_rows(lib):
     check_against_oracle(x[rows], g, to_np(y)[rows], to_np(q)[rows], to_np(sf)[rows])
 
 
+def test_rows_do_not_depend_on_batch(lib):
+    """Large batches take several rows per workgroup (the next row's x in flight while a row is written), small
+    ones one; a row's outputs are the same bits either way, in every output form."""
+    M = 8192 + 5                                         # a ragged last workgroup
+    x = si.quant_sweep_input(M)
+    g = si.rmsnorm_gamma(x.shape[1])
+    xd, gd = bf16_to_dev(x), bf16_to_dev(g)
+    y, q, sf = lib.mxfp8_rmsnorm_quantize(xd, gd, EPS, bf16_out=True)
+    q1, sf1 = lib.mxfp8_rmsnorm_quantize(xd, gd, EPS)
+    assert torch.equal(q1, q) and torch.equal(sf1, sf)
+    for lo, hi in ((0, 7), (4093, 4100), (M - 9, M)):
+        ys, qs, sfs = lib.mxfp8_rmsnorm_quantize(xd[lo:hi], gd, EPS, bf16_out=True)
+        assert torch.equal(ys, y[lo:hi]) and torch.equal(qs, q[lo:hi]) and torch.equal(sfs, sf[lo:hi]), (lo, hi)
+    rows = np.concatenate([np.arange(8), np.arange(M - 8, M)])
+    check_against_oracle(x[rows], g, to_np(y)[rows], to_np(q)[rows], to_np(sf)[rows])
+
+
 def test_special_rows(lib):
     """All-zero rows give zeros with scale byte 0; constant rows give exactly +-gamma (r * c is 1 up to an
     fp32 rounding, which BF16 absorbs for gamma values with short mantissas); one non-zero element gives
